@@ -1,0 +1,219 @@
+#!/usr/bin/env python3
+"""Benchmark of one query-aware sparse decode step on one MI355X.
+
+Workload (the headline setting): a Llama-7B-like attention layer at 32K
+context, B=1, Hq=Hkv=32, d=128, bf16 q/K/V ~ N(0,1) times per-channel scales
+U(0.5, 2), 8 planted needles per head, 16-token pages, a 2048-token budget
+(126 pages by score + sink page + recent page), Quest min/max scoring.
+
+A step = score every page -> exact top-K -> split-K attention over the kept
+pages (+ merge), i.e. one sa_decode_step call.  The page metadata is built
+once per layer copy beforehand (the insert-time update, not part of a step).
+Inputs are resident in HBM before timing starts.  R = 16 copies of the layer
+(8.7 GB) are rotated, and every step uses a fresh seeded query, so neither
+the 256 MB Infinity Cache nor a repeated selection can serve the reads.
+
+value = effective HBM GB/s of the step = algorithmic bytes (metadata of every
+page + K/V of the kept pages + q + out) / step time.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse decode-step µs + effective HBM GB/s (% of peak), 32K ctx, 2048-token budget"
+PEAK_GBS = 8000.0  # MI355X HBM3E
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--copies", type=int, default=16, help="layer copies rotated per step")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    return ap.parse_args()
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(this path has no multi-GPU part)", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import query_aware_sparse_min_amd as sa
+    import synth
+
+    if not os.path.exists(sa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    sa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    t0 = time.time()
+    wl = synth.make_config(2)
+    d = synth.to_device(wl, dev)
+    kv0 = sa.KVCache(d.k, d.v)
+    seqs = sa.Seqs(d.page_table, d.seq_lens)
+    cfg = sa.SelectCfg(sa.SA_MODE_QUEST, 16, wl.k_compete, wl.n_head_forced, wl.n_tail_forced)
+    R = max(1, args.copies)
+    copies = []
+    for r in range(R):
+        k = d.k if r == 0 else d.k.clone()
+        v = d.v if r == 0 else d.v.clone()
+        kv = sa.KVCache(k, v)
+        meta, _ = sa.alloc_meta(kv, cfg)
+        sa.sa_build_page_meta(kv, seqs, cfg, meta)
+        copies.append((kv, meta))
+    NQ = 64
+    qs = [synth.q_to_device(wl, synth.fresh_q(wl, i), dev) for i in range(NQ)]
+    ws = sa.alloc_workspace(sa.sa_decode_step_workspace_size(wl.Hq, kv0, seqs, cfg), dev)
+    out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    ms = sa.sa_max_selected(seqs, cfg)
+    torch.cuda.synchronize()
+    setup_s = time.time() - t0
+
+    def step(i):
+        kv, meta = copies[i % R]
+        sa.sa_decode_step(qs[i % NQ], kv, seqs, cfg, meta, None, wl.softmax_scale, out, ws)
+
+    stream = torch.cuda.current_stream()
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ev[0].record(stream)
+    for i in range(args.steps):
+        step(args.warmup + i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    total_ms = ev[0].elapsed_time(ev[-1])
+    per = np.array([ev[i].elapsed_time(ev[i + 1]) for i in range(args.steps)]) * 1e3  # us
+    ms_per_step = total_ms / args.steps
+
+    # algorithmic bytes: selection sizes are fixed by the budget (126 + 2 pages per head)
+    num = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)
+    sel = torch.empty((wl.B, wl.Hkv, ms), dtype=torch.int32, device=dev)
+    kv, meta = copies[0]
+    sa.sa_decode_step(qs[0], kv, seqs, cfg, meta, None, wl.softmax_scale, out, ws, sel, num)
+    torch.cuda.synchronize()
+    nb = synth.step_bytes(wl, num.cpu().numpy())
+    step_gbs = nb["total"] / (ms_per_step * 1e-3) / 1e9
+
+    # per-entry-point timing on the same stream (scorer / top-K / attention+merge)
+    mu = sa.sa_max_units(seqs, cfg)
+    scores = torch.empty((wl.B, wl.Hkv, mu), dtype=torch.float32, device=dev)
+    sels = []
+    for r in range(R):
+        kv, meta = copies[r]
+        s_r = torch.empty((wl.B, wl.Hkv, ms), dtype=torch.int32, device=dev)
+        n_r = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)
+        sa.sa_score_pages(qs[r], kv, seqs, cfg, meta, None, scores)
+        sa.sa_topk_pages(scores, wl.Hkv, seqs, cfg, s_r, n_r)
+        sels.append((s_r, n_r))
+    aws = sa.alloc_workspace(sa.sa_attn_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.max_pages, ms), dev)
+    dws = sa.alloc_workspace(sa.sa_attn_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.max_pages, 0), dev)
+    torch.cuda.synchronize()
+
+    def timed(fn, n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        for i in range(min(n, 10)):
+            fn(i)
+        torch.cuda.synchronize()
+        a.record(stream)
+        for i in range(n):
+            fn(i)
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3  # us per call
+
+    n_k = max(args.steps, 50)
+    score_us = timed(lambda i: sa.sa_score_pages(qs[i % R], copies[i % R][0], seqs, cfg,
+                                                 copies[i % R][1], None, scores), n_k)
+    topk_us = timed(lambda i: sa.sa_topk_pages(scores, wl.Hkv, seqs, cfg, sels[0][0], sels[0][1]), n_k)
+    attn_us = timed(lambda i: sa.sa_sparse_decode_attn(qs[i % R], copies[i % R][0], seqs,
+                                                       sels[i % R][0], sels[i % R][1],
+                                                       wl.softmax_scale, out, aws), n_k)
+    dense_us = timed(lambda i: sa.sa_sparse_decode_attn(qs[i % NQ], copies[i % R][0], seqs, None,
+                                                        None, wl.softmax_scale, out, dws),
+                     max(20, args.steps // 4))
+    dense_bytes = synth.dense_bytes(wl)
+    kernels = {
+        "score_pages": {"us": score_us, "bytes": nb["meta"] + nb["q"]},
+        "attention_merge": {"us": attn_us, "bytes": nb["kv"] + nb["q"] + nb["out"]},
+    }
+    dom_name = max(kernels, key=lambda k: kernels[k]["us"])
+    dom = kernels[dom_name]
+    dom_gbs = dom["bytes"] / (dom["us"] * 1e-6) / 1e9
+
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, args.cpu_seconds, nb["total"])
+
+    rec = {
+        "metric": METRIC,
+        "value": round(step_gbs, 1),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "input_dtype": "bf16",
+        "data": "synthetic (seeded N(0,1) x per-channel U(0.5,2), 8 needles/head)",
+        "config": {"workload": "Llama-7B-like layer decode, 32K context, 2048-token budget",
+                   "batch": wl.B, "num_q_heads": wl.Hq, "num_kv_heads": wl.Hkv, "head_dim": wl.d,
+                   "context": int(wl.seq_lens[0]), "page_size": 16, "budget_pages": ms,
+                   "scoring": "quest min/max bound", "layer_copies_rotated": R},
+        "step_us": round(ms_per_step * 1e3, 2),
+        "step_us_p10_p50_p90": [round(float(np.percentile(per, p)), 2) for p in (10, 50, 90)],
+        "step_bytes": nb["total"],
+        "hbm_peak_frac": round(step_gbs / PEAK_GBS, 4),
+        "dense_us": round(dense_us, 2),
+        "dense_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
+        "speedup_vs_dense": round(dense_us / (ms_per_step * 1e3), 2),
+        "phase_us": {"score_pages": round(score_us, 2), "topk_pages": round(topk_us, 2),
+                     "attention_merge": round(attn_us, 2)},
+        "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1),
+                     "peak": PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_GBS, 4),
+                     "traffic": None},
+        "cpu_baseline": cpu,
+        "setup_s": round(setup_s, 1),
+    }
+    print(json.dumps(rec), flush=True)
+
+
+def cpu_baseline(wl, seconds, step_bytes):
+    """The oracle's decode step on the host, on as many fresh queries as fit in ~seconds."""
+    import oracle
+    import synth
+
+    meta, _ = oracle.build_meta(wl)  # amortised, like the GPU's metadata build
+    n, t_used = 0, 0.0
+    while n < 400 and (t_used < seconds or n == 0):
+        q = synth.fresh_q(wl, n)
+        t = time.perf_counter()
+        oracle.decode_step(wl, meta, None, q=q)
+        t_used += time.perf_counter() - t
+        n += 1
+    per_step = t_used / n
+    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
+            "kind": "oracle", "step_ms": round(per_step * 1e3, 1),
+            "sample": f"{n} full decode steps of the same workload (all 32 heads), fresh query each"}
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,304 @@
+// sa_api.hip - the extern "C" boundary: argument validation, buffer sizing and
+// launch planning, then the kernels of sa_meta / sa_score / sa_topk / sa_attn.
+// Every check runs on the host before anything is enqueued, and no function
+// allocates, frees or synchronises.
+#include <string.h>
+
+#include "sa_internal.h"
+
+using namespace sa;
+
+namespace {
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+bool aligned16(const void* p) { return ((uintptr_t)p & 15u) == 0; }
+
+int check_kv(const sa_kv_cache* kv) {
+  if (!kv || !kv->k || !kv->v) return SA_ERR_INVALID_ARG;
+  if (kv->dtype != SA_F32 && kv->dtype != SA_BF16 && kv->dtype != SA_I8) return SA_ERR_INVALID_ARG;
+  if (kv->dtype == SA_I8 && (!kv->k_scale || !kv->v_scale)) return SA_ERR_INVALID_ARG;
+  if (kv->num_pages < 1 || kv->num_kv_heads < 1 || kv->num_kv_heads > 65535) return SA_ERR_INVALID_ARG;
+  if (kv->page_size != kPage || kv->head_dim != kHeadDim) return SA_ERR_UNSUPPORTED;
+  if (!aligned16(kv->k) || !aligned16(kv->v)) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
+int check_seqs(const sa_seqs* s) {
+  if (!s || !s->page_table || !s->seq_lens) return SA_ERR_INVALID_ARG;
+  if (s->batch < 1 || s->batch > 65535 || s->max_pages < 1) return SA_ERR_INVALID_ARG;
+  if ((long long)s->max_pages * kPage > 0x3FFFFFFFLL) return SA_ERR_INVALID_ARG;
+  return SA_OK;
+}
+
+// Fields that selection alone uses (sa_topk_pages, list sizes).
+int check_select(const sa_select_cfg* c) {
+  if (!c) return SA_ERR_INVALID_ARG;
+  if (c->mode != SA_MODE_QUEST && c->mode != SA_MODE_SALS) return SA_ERR_INVALID_ARG;
+  if (c->k_compete < 0 || c->n_head_forced < 0 || c->n_tail_forced < 0) return SA_ERR_INVALID_ARG;
+  if ((long long)c->k_compete + c->n_head_forced + c->n_tail_forced < 1) return SA_ERR_INVALID_ARG;
+  if ((long long)c->k_compete + c->n_head_forced + c->n_tail_forced > 0x3FFFFFFLL) return SA_ERR_INVALID_ARG;
+  if (c->unit_tokens < kPage || c->unit_tokens % kPage != 0) return SA_ERR_INVALID_ARG;
+  if (c->mode == SA_MODE_QUEST && c->unit_tokens != kPage) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+// Everything scoring needs as well.
+int check_cfg(const sa_select_cfg* c) {
+  const int rc = check_select(c);
+  if (rc != SA_OK) return rc;
+  if (c->mode == SA_MODE_SALS) {
+    if (!c->proj) return SA_ERR_INVALID_ARG;
+    if (c->rank != kRank) return SA_ERR_UNSUPPORTED;
+    if (!(c->lse_scale == c->lse_scale)) return SA_ERR_INVALID_ARG;  // NaN
+  }
+  return SA_OK;
+}
+
+// query heads per kv-head supported by the kernels
+bool group_ok(int hq, int hkv) {
+  if (hq < 1 || hkv < 1 || hq % hkv != 0) return false;
+  const int G = hq / hkv;
+  return G == 1 || G == 2 || G == 4 || G == 8 || G == 16;
+}
+
+int check_q(const void* q, int q_dtype, int hq, int hkv) {
+  if (!q || !aligned16(q)) return SA_ERR_INVALID_ARG;
+  if (q_dtype != SA_F32 && q_dtype != SA_BF16) return SA_ERR_INVALID_ARG;
+  if (hq < 1 || hq % hkv != 0) return SA_ERR_INVALID_ARG;
+  if (!group_ok(hq, hkv)) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+int check_mode_kv(const sa_select_cfg* c, const sa_kv_cache* kv) {
+  if (c->mode == SA_MODE_QUEST && kv->dtype == SA_I8) return SA_ERR_UNSUPPORTED;
+  if (c->mode == SA_MODE_SALS && (64 % kv->num_kv_heads != 0)) return SA_ERR_UNSUPPORTED;
+  return SA_OK;
+}
+
+int max_units_of(const sa_seqs* s, const sa_select_cfg* c) {
+  return (int)(((long long)s->max_pages * kPage + c->unit_tokens - 1) / c->unit_tokens);
+}
+
+int max_sel_of(const sa_seqs* s, const sa_select_cfg* c) {
+  const long long u = (long long)c->k_compete + c->n_head_forced + c->n_tail_forced;
+  const long long pages = u * (c->unit_tokens / kPage);
+  return (int)(pages < s->max_pages ? pages : s->max_pages);
+}
+
+int hip_status(hipError_t e) { return e == hipSuccess ? SA_OK : SA_ERR_HIP; }
+
+Shapes shapes_of(int hq, const sa_kv_cache* kv, const sa_seqs* s) {
+  return Shapes{s->batch, hq, kv->num_kv_heads, s->max_pages, kv->num_pages};
+}
+
+struct StepLayout {
+  size_t scores, sel, num_sel, partials, total;
+  int max_units, max_sel;
+  bool dense;
+  AttnPlan plan;
+};
+
+StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa_select_cfg* c) {
+  StepLayout L{};
+  L.max_units = max_units_of(s, c);
+  L.max_sel = max_sel_of(s, c);
+  // every list keeps all of its units: no scoring needed
+  L.dense = (long long)c->k_compete + c->n_head_forced + c->n_tail_forced >= L.max_units;
+  const size_t lists = (size_t)s->batch * kv->num_kv_heads;
+  L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel);
+  size_t off = 0;
+  L.scores = off;
+  off = align_up(off + (L.dense ? 0 : lists * L.max_units * sizeof(float)));
+  L.sel = off;
+  off = align_up(off + lists * L.max_sel * sizeof(int32_t));
+  L.num_sel = off;
+  off = align_up(off + lists * sizeof(int32_t));
+  L.partials = off;
+  off = align_up(off + L.plan.partial_floats * sizeof(float));
+  L.total = off;
+  return L;
+}
+
+}  // namespace
+
+extern "C" {
+
+int sa_version(void) { return 1; }
+
+const char* sa_status_string(int status) {
+  switch (status) {
+    case SA_OK: return "ok";
+    case SA_ERR_INVALID_ARG: return "invalid argument";
+    case SA_ERR_UNSUPPORTED: return "unsupported configuration";
+    case SA_ERR_WORKSPACE_TOO_SMALL: return "workspace too small";
+    case SA_ERR_HIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+size_t sa_meta_bytes(const sa_kv_cache* kv, const sa_select_cfg* cfg) {
+  if (check_kv(kv) != SA_OK || check_cfg(cfg) != SA_OK) return 0;
+  if (cfg->mode == SA_MODE_QUEST) {
+    if (kv->dtype == SA_I8) return 0;
+    const size_t es = kv->dtype == SA_F32 ? 4 : 2;
+    return (size_t)kv->num_pages * kv->num_kv_heads * 2 * kHeadDim * es;
+  }
+  return (size_t)kv->num_pages * kPage * kv->num_kv_heads * (kRank / 2);
+}
+
+size_t sa_meta_scale_bytes(const sa_kv_cache* kv, const sa_select_cfg* cfg) {
+  if (check_kv(kv) != SA_OK || check_cfg(cfg) != SA_OK) return 0;
+  if (cfg->mode == SA_MODE_QUEST) return 0;
+  return (size_t)kv->num_pages * kPage * kv->num_kv_heads * sizeof(uint16_t);
+}
+
+int32_t sa_max_units(const sa_seqs* seqs, const sa_select_cfg* cfg) {
+  if (check_seqs(seqs) != SA_OK || check_select(cfg) != SA_OK) return 0;
+  return max_units_of(seqs, cfg);
+}
+
+int32_t sa_max_selected(const sa_seqs* seqs, const sa_select_cfg* cfg) {
+  if (check_seqs(seqs) != SA_OK || check_select(cfg) != SA_OK) return 0;
+  return max_sel_of(seqs, cfg);
+}
+
+int sa_build_page_meta(const sa_kv_cache* kv, const sa_seqs* seqs, const sa_select_cfg* cfg,
+                       void* meta, uint16_t* meta_scale, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs)) || (rc = check_cfg(cfg))) return rc;
+  if ((rc = check_mode_kv(cfg, kv))) return rc;
+  if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
+  const Shapes s = shapes_of(kv->num_kv_heads, kv, seqs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg->mode == SA_MODE_QUEST)
+    return hip_status(launch_quest_meta(kv->dtype, kv->k, s, seqs->page_table, seqs->seq_lens, meta, st));
+  if (!meta_scale) return SA_ERR_INVALID_ARG;
+  return hip_status(launch_sals_index(kv->dtype, kv->k, kv->k_scale, s, seqs->page_table,
+                                      seqs->seq_lens, cfg->proj, static_cast<uint8_t*>(meta),
+                                      meta_scale, st));
+}
+
+int sa_score_pages(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache* kv,
+                   const sa_seqs* seqs, const sa_select_cfg* cfg, const void* meta,
+                   const uint16_t* meta_scale, float* scores, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs)) || (rc = check_cfg(cfg))) return rc;
+  if ((rc = check_q(q, q_dtype, num_q_heads, kv->num_kv_heads))) return rc;
+  if ((rc = check_mode_kv(cfg, kv))) return rc;
+  if (!meta || !aligned16(meta) || !scores) return SA_ERR_INVALID_ARG;
+  const Shapes s = shapes_of(num_q_heads, kv, seqs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg->mode == SA_MODE_QUEST)
+    return hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
+                                         seqs->seq_lens, scores, st));
+  if (!meta_scale) return SA_ERR_INVALID_ARG;
+  return hip_status(launch_sals_score(q_dtype, q, static_cast<const uint8_t*>(meta), meta_scale,
+                                      cfg->proj, s, seqs->page_table, seqs->seq_lens,
+                                      cfg->unit_tokens, cfg->lse_scale, scores,
+                                      max_units_of(seqs, cfg), st));
+}
+
+int sa_topk_pages(const float* scores, int32_t num_kv_heads, const sa_seqs* seqs,
+                  const sa_select_cfg* cfg, int32_t* sel, int32_t* num_sel, void* stream) {
+  int rc;
+  if ((rc = check_seqs(seqs)) || (rc = check_select(cfg))) return rc;
+  if (!scores || !sel || !num_sel || num_kv_heads < 1 || num_kv_heads > 65535) return SA_ERR_INVALID_ARG;
+  const Shapes s{seqs->batch, num_kv_heads, num_kv_heads, seqs->max_pages, 0};
+  return hip_status(launch_topk(scores, max_units_of(seqs, cfg), s, seqs->seq_lens,
+                                cfg->unit_tokens, cfg->k_compete, cfg->n_head_forced,
+                                cfg->n_tail_forced, sel, num_sel, max_sel_of(seqs, cfg),
+                                static_cast<hipStream_t>(stream)));
+}
+
+size_t sa_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                              int32_t max_pages, int32_t max_sel) {
+  if (batch < 1 || max_pages < 1 || !group_ok(num_q_heads, num_kv_heads)) return 0;
+  const AttnPlan p = plan_attention(batch, num_q_heads, num_kv_heads, max_sel > 0 ? max_sel : max_pages);
+  return align_up(p.partial_floats * sizeof(float));
+}
+
+int sa_sparse_decode_attn(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                          const sa_kv_cache* kv, const sa_seqs* seqs, const int32_t* sel,
+                          const int32_t* num_sel, int32_t max_sel, float softmax_scale, float* out,
+                          void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs))) return rc;
+  if ((rc = check_q(q, q_dtype, num_q_heads, kv->num_kv_heads))) return rc;
+  if (!out || !workspace || ((uintptr_t)workspace % kAlign) != 0) return SA_ERR_INVALID_ARG;
+  if ((sel == nullptr) != (num_sel == nullptr)) return SA_ERR_INVALID_ARG;
+  if (sel && max_sel < 1) return SA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
+  const int list_len = sel ? max_sel : seqs->max_pages;
+  const AttnPlan plan = plan_attention(seqs->batch, num_q_heads, kv->num_kv_heads, list_len);
+  if (workspace_bytes < plan.partial_floats * sizeof(float)) return SA_ERR_WORKSPACE_TOO_SMALL;
+  const Shapes s = shapes_of(num_q_heads, kv, seqs);
+  return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale, kv->v_scale,
+                                     s, seqs->page_table, seqs->seq_lens, sel, num_sel,
+                                     sel ? max_sel : 0, plan, softmax_scale,
+                                     static_cast<float*>(workspace), out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache* kv,
+                                     const sa_seqs* seqs, const sa_select_cfg* cfg) {
+  if (check_kv(kv) || check_seqs(seqs) || check_cfg(cfg)) return 0;
+  if (!group_ok(num_q_heads, kv->num_kv_heads)) return 0;
+  return step_layout(num_q_heads, kv, seqs, cfg).total;
+}
+
+int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache* kv,
+                   const sa_seqs* seqs, const sa_select_cfg* cfg, const void* meta,
+                   const uint16_t* meta_scale, float softmax_scale, float* out, int32_t* sel,
+                   int32_t* num_sel, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs)) || (rc = check_cfg(cfg))) return rc;
+  if ((rc = check_q(q, q_dtype, num_q_heads, kv->num_kv_heads))) return rc;
+  if ((rc = check_mode_kv(cfg, kv))) return rc;
+  if (!out || !workspace || ((uintptr_t)workspace % kAlign) != 0) return SA_ERR_INVALID_ARG;
+  if ((sel == nullptr) != (num_sel == nullptr)) return SA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
+  const StepLayout lay = step_layout(num_q_heads, kv, seqs, cfg);
+  if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+  if (!lay.dense) {
+    if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
+    if (cfg->mode == SA_MODE_SALS && !meta_scale) return SA_ERR_INVALID_ARG;
+  }
+  char* ws = static_cast<char*>(workspace);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  const Shapes s = shapes_of(num_q_heads, kv, seqs);
+  int32_t* sel_buf = sel ? sel : reinterpret_cast<int32_t*>(ws + lay.sel);
+  int32_t* num_buf = num_sel ? num_sel : reinterpret_cast<int32_t*>(ws + lay.num_sel);
+  float* partials = reinterpret_cast<float*>(ws + lay.partials);
+
+  if (lay.dense) {
+    // every unit of every list is kept: selection is the identity
+    if (sel) {
+      rc = hip_status(launch_topk(nullptr, lay.max_units, s, seqs->seq_lens, cfg->unit_tokens,
+                                  cfg->k_compete, cfg->n_head_forced, cfg->n_tail_forced, sel_buf,
+                                  num_buf, lay.max_sel, st));
+      if (rc) return rc;
+    }
+    return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale,
+                                       kv->v_scale, s, seqs->page_table, seqs->seq_lens, nullptr,
+                                       nullptr, 0, lay.plan, softmax_scale, partials, out, st));
+  }
+  float* scores = reinterpret_cast<float*>(ws + lay.scores);
+  if (cfg->mode == SA_MODE_QUEST)
+    rc = hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
+                                       seqs->seq_lens, scores, st));
+  else
+    rc = hip_status(launch_sals_score(q_dtype, q, static_cast<const uint8_t*>(meta), meta_scale,
+                                      cfg->proj, s, seqs->page_table, seqs->seq_lens,
+                                      cfg->unit_tokens, cfg->lse_scale, scores, lay.max_units, st));
+  if (rc) return rc;
+  rc = hip_status(launch_topk(scores, lay.max_units, s, seqs->seq_lens, cfg->unit_tokens,
+                              cfg->k_compete, cfg->n_head_forced, cfg->n_tail_forced, sel_buf,
+                              num_buf, lay.max_sel, st));
+  if (rc) return rc;
+  return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale, kv->v_scale,
+                                     s, seqs->page_table, seqs->seq_lens, sel_buf, num_buf,
+                                     lay.max_sel, lay.plan, softmax_scale, partials, out, st));
+}
+
+}  // extern "C"

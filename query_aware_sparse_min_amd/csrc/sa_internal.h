@@ -1,0 +1,101 @@
+// sa_internal.h - shared device helpers and launcher declarations of the
+// gfx950 sparse decode-attention library.  Not a public header.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "sa.h"
+
+namespace sa {
+
+constexpr int kPage = 16;      // tokens per page
+constexpr int kHeadDim = 128;  // head dimension
+constexpr int kRank = 16;      // SALS index-key width
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.69314718055994531f;
+
+// ------------------------------------------------------------ conversions
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  return (float)__builtin_bit_cast(_Float16, h);
+}
+
+// Eight consecutive elements of a K/V/metadata row as fp32 (exact widening).
+// DT: SA_F32 | SA_BF16 | SA_I8 (int8 returns the integer codes as floats).
+template <int DT>
+__device__ __forceinline__ void load8(const void* base, size_t elem, float (&x)[8]) {
+  if constexpr (DT == SA_F32) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + elem);
+    float4 a = p[0], b = p[1];
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w;
+    x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  } else if constexpr (DT == SA_BF16) {
+    uint4 w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + elem);
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  } else {
+    uint2 w = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(base) + elem);
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      x[e] = (float)(int8_t)(w.x >> (8 * e));
+      x[4 + e] = (float)(int8_t)(w.y >> (8 * e));
+    }
+  }
+}
+
+__device__ __forceinline__ int clamp_len(int L, int max_pages) {
+  return L < 0 ? 0 : (L > max_pages * kPage ? max_pages * kPage : L);
+}
+
+// --------------------------------------------------------- wave reductions
+template <int MASK>
+__device__ __forceinline__ float xor_sum(float v) {
+  return v + __shfl_xor(v, MASK, 64);
+}
+template <int MASK>
+__device__ __forceinline__ float xor_max(float v) {
+  return fmaxf(v, __shfl_xor(v, MASK, 64));
+}
+
+// ------------------------------------------------------------ launchers
+// Every launcher enqueues on 'stream' and returns hipGetLastError() of the launch.
+struct Shapes {
+  int B, Hq, Hkv, max_pages, num_pages;
+};
+
+hipError_t launch_quest_meta(int dtype, const void* k, const Shapes& s, const int32_t* pt,
+                             const int32_t* lens, void* meta, hipStream_t st);
+hipError_t launch_sals_index(int dtype, const void* k, const uint16_t* k_scale, const Shapes& s,
+                             const int32_t* pt, const int32_t* lens, const float* proj,
+                             uint8_t* codes, uint16_t* scales, hipStream_t st);
+hipError_t launch_quest_score(int kv_dtype, int q_dtype, const void* q, const void* meta,
+                              const Shapes& s, const int32_t* pt, const int32_t* lens,
+                              float* scores, hipStream_t st);
+hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,
+                             const uint16_t* scales, const float* proj, const Shapes& s,
+                             const int32_t* pt, const int32_t* lens, int unit_tokens, float tau,
+                             float* scores, int max_units, hipStream_t st);
+hipError_t launch_topk(const float* scores, int max_units, const Shapes& s, const int32_t* lens,
+                       int unit_tokens, int k, int n_head, int n_tail, int32_t* sel,
+                       int32_t* num_sel, int max_sel, hipStream_t st);
+
+struct AttnPlan {
+  int list_len;   // pages per (b, kv-head) list the kernel may visit
+  int pps;        // pages per split
+  int nsplit;     // splits per list
+  size_t partial_floats;  // workspace floats
+};
+AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len);
+
+hipError_t launch_attention(int kv_dtype, int q_dtype, const void* q, const void* k,
+                            const void* v, const uint16_t* k_scale, const uint16_t* v_scale,
+                            const Shapes& s, const int32_t* pt, const int32_t* lens,
+                            const int32_t* sel, const int32_t* num_sel, int max_sel,
+                            const AttnPlan& plan, float softmax_scale, float* partials,
+                            float* out, hipStream_t st);
+
+}  // namespace sa

@@ -434,3 +434,51 @@ def dense_bytes(wl: Workload) -> int:
     npages = sum(wl.n_pages(b) for b in range(wl.B))
     per_page = PAGE * wl.d * e * 2 + (PAGE * 2 * 2 if wl.kv_dtype == "i8" else 0)
     return npages * wl.Hkv * per_page + wl.B * wl.Hq * wl.d * (_elt(wl.q_dtype) + 4)
+
+
+# ----------------------------------------------------------------------------
+# device copies (torch used only as an allocator)
+# ----------------------------------------------------------------------------
+def _to_torch(a: Optional[np.ndarray], kind: str, device):
+    import torch
+    if a is None:
+        return None
+    a = np.ascontiguousarray(a)
+    if kind == "bf16":
+        t = torch.from_numpy(a.view(np.int16)).view(torch.bfloat16)
+    elif kind == "f16bits":
+        t = torch.from_numpy(a.view(np.int16))
+    else:
+        t = torch.from_numpy(a)
+    return t.to(device, non_blocking=False)
+
+
+@dataclass
+class DeviceWorkload:
+    q: object
+    k: object
+    v: object
+    k_scale: object
+    v_scale: object
+    page_table: object
+    seq_lens: object
+    proj: object
+
+
+def to_device(wl: Workload, device="cuda", q: Optional[np.ndarray] = None) -> DeviceWorkload:
+    """Copy a workload's arrays to device tensors of matching dtypes (bf16 bits -> torch.bfloat16,
+    fp16 scale bits -> torch.int16)."""
+    q = wl.q if q is None else q
+    kvk = "bf16" if wl.kv_dtype == "bf16" else "raw"
+    return DeviceWorkload(
+        q=_to_torch(q, "bf16" if wl.q_dtype == "bf16" else "raw", device),
+        k=_to_torch(wl.k, kvk, device), v=_to_torch(wl.v, kvk, device),
+        k_scale=_to_torch(wl.k_scale, "f16bits", device),
+        v_scale=_to_torch(wl.v_scale, "f16bits", device),
+        page_table=_to_torch(wl.page_table, "raw", device),
+        seq_lens=_to_torch(wl.seq_lens, "raw", device),
+        proj=_to_torch(wl.proj, "raw", device))
+
+
+def q_to_device(wl: Workload, q: np.ndarray, device="cuda"):
+    return _to_torch(q, "bf16" if wl.q_dtype == "bf16" else "raw", device)

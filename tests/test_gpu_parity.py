@@ -1,0 +1,220 @@
+"""GPU-vs-oracle parity of every step through the C ABI, on small seeded
+workloads that span several tiles and ragged tails (run on an MI355X)."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+import synth
+from sa_testlib import (GpuCase, attn_tol, check_attention, check_scores, check_selection,
+                        meta_np, oracle_rows_for_lists)
+
+pytestmark = pytest.mark.gpu
+
+CASES = {
+    "mha_f32": dict(B=1, Hq=8, Hkv=8, lens=(2048,), kv_dtype="f32", q_dtype="f32", budget_pages=16),
+    "mha_bf16_ragged": dict(B=3, Hq=4, Hkv=4, lens=(1000, 17, 3333), kv_dtype="bf16",
+                            q_dtype="bf16", budget_pages=24, page_table="random"),
+    "gqa2_bf16kv_f32q": dict(B=2, Hq=8, Hkv=4, lens=(1500, 700), kv_dtype="bf16", q_dtype="f32",
+                             budget_pages=20, page_table="random"),
+    "gqa4_bf16": dict(B=4, Hq=16, Hkv=4, lens=(3000, 300, 2047, 1025), kv_dtype="bf16",
+                      q_dtype="bf16", budget_pages=32, page_table="random"),
+    "gqa8_bf16": dict(B=2, Hq=16, Hkv=2, lens=(4096, 2500), kv_dtype="bf16", q_dtype="bf16",
+                      budget_pages=40),
+    "gqa16_bf16": dict(B=1, Hq=32, Hkv=2, lens=(2222,), kv_dtype="bf16", q_dtype="bf16",
+                       budget_pages=20),
+    "gqa4_f32": dict(B=2, Hq=8, Hkv=2, lens=(900, 1601), kv_dtype="f32", q_dtype="f32",
+                     budget_pages=12, page_table="random"),
+    "sals_i8": dict(B=2, Hq=8, Hkv=2, lens=(5000, 700), kv_dtype="i8", q_dtype="bf16", mode="sals",
+                    k_compete=8, page_table="random"),
+    "sals_bf16": dict(B=2, Hq=32, Hkv=8, lens=(4100, 1000), kv_dtype="bf16", q_dtype="bf16",
+                      mode="sals", k_compete=6),
+    "sals_f32_h1": dict(B=1, Hq=4, Hkv=1, lens=(3000,), kv_dtype="f32", q_dtype="f32",
+                        mode="sals", k_compete=5),
+    "sals_i8_h16": dict(B=1, Hq=16, Hkv=16, lens=(2100,), kv_dtype="i8", q_dtype="bf16",
+                        mode="sals", k_compete=4),
+}
+
+
+def _full_check(wl, label):
+    print(f"[gpu] case {label}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} lens={list(wl.seq_lens)} "
+          f"kv={wl.kv_dtype} mode={wl.mode}", flush=True)
+    c = GpuCase(wl)
+    c.build_meta()
+    o_meta, o_ms = oracle.build_meta(wl)
+    g_meta, g_ms = meta_np(c)
+    # metadata / index key: bit-exact on every referenced page
+    for b in range(wl.B):
+        pages = wl.page_table[b, :wl.n_pages(b)]
+        assert np.array_equal(g_meta[pages].view(np.uint8), o_meta[pages].view(np.uint8)), \
+            f"metadata differs (b={b})"
+        if o_ms is not None:
+            assert np.array_equal(g_ms[pages], o_ms[pages]), f"index scales differ (b={b})"
+    # scores
+    g_sc_t = c.scores()
+    g_sc = g_sc_t.cpu().numpy()
+    o_sc, o_ab = oracle.score(wl, o_meta, o_ms)
+    check_scores(wl, g_sc, o_sc, o_ab)
+    # selection on identical (GPU) scores: bit-exact
+    g_sel_t, g_num_t = c.topk(g_sc_t)
+    g_sel, g_num = g_sel_t.cpu().numpy(), g_num_t.cpu().numpy()
+    r_sel, r_num = oracle.select(np.where(np.isnan(g_sc), -np.inf, g_sc).astype(np.float64),
+                                 wl.seq_lens, wl.unit_tokens, wl.k_compete, wl.n_head_forced,
+                                 wl.n_tail_forced, wl.max_sel)
+    assert np.array_equal(g_num, r_num) and np.array_equal(g_sel, r_sel), "top-K differs on identical scores"
+    # selection vs the oracle's own scores
+    o_sel, o_num = oracle.select(o_sc, wl.seq_lens, wl.unit_tokens, wl.k_compete, wl.n_head_forced,
+                                 wl.n_tail_forced, wl.max_sel)
+    swapped = check_selection(wl, g_sel, g_num, o_sel, o_num, o_sc, o_ab)
+    # attention on the oracle's selection
+    o_out = oracle.attention(wl.q, wl.q_dtype, wl.k, wl.v, wl.kv_dtype, wl.k_scale, wl.v_scale,
+                             wl.page_table, wl.seq_lens, o_sel, o_num, wl.softmax_scale)
+    g_out = c.attention(torch.from_numpy(o_sel).to(c.dev), torch.from_numpy(o_num).to(c.dev))
+    e_attn = check_attention(wl, g_out.cpu().numpy(), o_out, what="sparse attention")
+    # fused step: rows of lists whose selection matches the oracle's are compared with the
+    # oracle; lists with a permitted near-tie swap are compared with the GPU attention kernel
+    # run on the step's own selection
+    s_out, s_sel, s_num = c.step()
+    s_out, s_sel, s_num = s_out.cpu().numpy(), s_sel.cpu().numpy(), s_num.cpu().numpy()
+    assert np.array_equal(s_sel, g_sel) and np.array_equal(s_num, g_num), "step selection differs"
+    keep = [(b, h) for b in range(wl.B) for h in range(wl.Hkv) if (b, h) not in swapped]
+    rows = oracle_rows_for_lists(wl, keep)
+    if len(rows):
+        check_attention(wl, s_out, o_out.reshape(-1, wl.d)[rows], rows=rows, what="decode step")
+    if swapped:
+        rows2 = oracle_rows_for_lists(wl, swapped)
+        ref = c.attention(torch.from_numpy(s_sel).to(c.dev), torch.from_numpy(s_num).to(c.dev))
+        assert np.array_equal(s_out.reshape(-1, wl.d)[rows2], ref.cpu().numpy().reshape(-1, wl.d)[rows2])
+    print(f"[gpu] case {label}: ok (attn err {e_attn:.2e}, swapped lists {len(swapped)})", flush=True)
+    return c
+
+
+@pytest.mark.parametrize("label", sorted(CASES))
+def test_step_parity(label):
+    wl = synth.make_custom(**CASES[label], seed=40 + sorted(CASES).index(label), name=label)
+    _full_check(wl, label)
+
+
+@pytest.mark.parametrize("lens,budget", [((1,), 16), ((16,), 16), ((17,), 2), ((15, 33, 48), 2),
+                                         ((300,), 2), ((16 * 40 + 1,), 3)])
+def test_short_and_edge_lengths(lens, budget):
+    wl = synth.make_custom(B=len(lens), Hq=4, Hkv=2, lens=lens, kv_dtype="bf16", q_dtype="bf16",
+                           budget_pages=budget, page_table="random", seed=3)
+    _full_check(wl, f"edge{lens}/{budget}")
+
+
+def test_only_forced_units():
+    wl = synth.make_custom(B=2, Hq=8, Hkv=4, lens=(1111, 640), kv_dtype="bf16", q_dtype="bf16",
+                           k_compete=0, page_table="random", seed=5)
+    _full_check(wl, "k0")
+
+
+def test_sals_with_sink_and_partial_last_block():
+    wl = synth.make_custom(B=2, Hq=8, Hkv=4, lens=(64 * 30 + 20, 64 * 3 + 1), kv_dtype="i8",
+                           q_dtype="bf16", mode="sals", k_compete=3, n_head_forced=1,
+                           n_tail_forced=1, seed=6)
+    _full_check(wl, "sals_sink")
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16", "i8"])
+def test_dense_attention_matches_oracle(kv_dtype):
+    wl = synth.make_custom(B=3, Hq=8, Hkv=2, lens=(2000, 1, 777), kv_dtype=kv_dtype,
+                           q_dtype="bf16", page_table="random", seed=8,
+                           mode="sals" if kv_dtype == "i8" else "quest")
+    print(f"[gpu] dense attention {kv_dtype}", flush=True)
+    c = GpuCase(wl)
+    g = c.attention(None, None).cpu().numpy()
+    o = oracle.attention(wl.q, wl.q_dtype, wl.k, wl.v, wl.kv_dtype, wl.k_scale, wl.v_scale,
+                         wl.page_table, wl.seq_lens, None, None, wl.softmax_scale)
+    check_attention(wl, g, o, what="dense attention")
+
+
+def test_all_pages_budget_equals_dense():
+    """Budget >= every unit: the step skips scoring and equals dense attention."""
+    wl = synth.make_custom(B=2, Hq=16, Hkv=4, lens=(3000, 2000), kv_dtype="bf16", q_dtype="bf16",
+                           budget_pages=10 ** 4, page_table="random", seed=9)
+    c = GpuCase(wl)
+    c.build_meta()
+    out, sel, num = c.step()
+    dense = c.attention(None, None)
+    assert torch.equal(out, dense)
+    for b in range(2):
+        assert np.all(num.cpu().numpy()[b] == wl.n_pages(b))
+    o = oracle.attention(wl.q, wl.q_dtype, wl.k, wl.v, wl.kv_dtype, None, None, wl.page_table,
+                         wl.seq_lens, None, None, wl.softmax_scale)
+    check_attention(wl, out.cpu().numpy(), o, what="all-pages step")
+
+
+def test_repeated_runs_are_bit_identical():
+    wl = synth.make_custom(B=2, Hq=16, Hkv=4, lens=(5000, 3000), kv_dtype="bf16", q_dtype="bf16",
+                           budget_pages=64, page_table="random", seed=10)
+    c = GpuCase(wl)
+    c.build_meta()
+    o1, s1, n1 = c.step()
+    o2, s2, n2 = c.step()
+    assert torch.equal(s1, s2) and torch.equal(n1, n2)
+    assert torch.equal(o1.view(torch.int32), o2.view(torch.int32))
+
+
+@pytest.mark.parametrize("kv_dtype", ["f32", "bf16"])
+def test_strong_needle_is_selected(kv_dtype):
+    """A needle whose true dot beats every other page's bound must be selected."""
+    wl = synth.make_custom(B=1, Hq=4, Hkv=4, lens=(16 * 200 - 5,), kv_dtype=kv_dtype,
+                           q_dtype=kv_dtype, budget_pages=4, seed=12)
+    o_meta, _ = oracle.build_meta(wl)
+    sc, _ = oracle.score(wl, o_meta, None)
+    n = wl.n_pages(0)
+    Q = (synth.bf16_to_f32(wl.q) if kv_dtype == "bf16" else wl.q).astype(np.float64)
+    pages = synth.uniform_int(1, 77, 4, 1, n - 2)
+    for h in range(4):
+        p = int(pages[h])
+        others = np.delete(sc[0, h, 1:n - 1], p - 1)
+        qn = np.linalg.norm(Q[0, h])
+        key = (1.25 * max(others.max(), 1e-3) / qn * Q[0, h] / qn).astype(np.float32)
+        wl.k[p, 3, h] = key if kv_dtype == "f32" else synth.f32_to_bf16(key)
+    c = GpuCase(wl)
+    c.build_meta()
+    _, sel, num = c.step()
+    sel, num = sel.cpu().numpy(), num.cpu().numpy()
+    for h in range(4):
+        assert int(pages[h]) in sel[0, h, :num[0, h]]
+
+
+# ---------------------------------------------------------------- top-K alone
+def _topk_case(lens, mu, k, fh, ft, ut, scores):
+    import query_aware_sparse_min_amd as sa
+    dev = torch.device("cuda")
+    B = len(lens)
+    max_pages = -(-mu * ut // 16)
+    lens = np.array([min(L, max_pages * 16) for L in lens], dtype=np.int32)
+    seqs = sa.Seqs(torch.zeros((B, max_pages), dtype=torch.int32, device=dev),
+                   torch.from_numpy(lens).to(dev))
+    cfg = sa.SelectCfg(sa.SA_MODE_QUEST if ut == 16 else sa.SA_MODE_SALS, ut, k, fh, ft)
+    ms = sa.sa_max_selected(seqs, cfg)
+    sel = torch.full((B, 1, ms), -7, dtype=torch.int32, device=dev)
+    num = torch.full((B, 1), -7, dtype=torch.int32, device=dev)
+    sa.sa_topk_pages(torch.from_numpy(scores.astype(np.float32)).to(dev), 1, seqs, cfg, sel, num)
+    o_sel, o_num = oracle.select(scores.astype(np.float32).astype(np.float64), lens, ut, k, fh, ft, ms)
+    assert np.array_equal(num.cpu().numpy(), o_num)
+    assert np.array_equal(sel.cpu().numpy(), o_sel)
+
+
+@pytest.mark.parametrize("n,k", [(40, 5), (3000, 126), (16384, 254), (20000, 300), (5000, 4990)])
+def test_topk_bit_exact_with_ties(n, k):
+    rng = np.random.default_rng(n)
+    vals = np.array([-3.0, -0.0, 0.0, 1.5, 1.5000001, 7.0, -np.inf], dtype=np.float32)
+    sc = rng.choice(vals, size=(2, 1, n)).astype(np.float32)
+    sc[1, 0] = rng.standard_normal(n).astype(np.float32)
+    sc[1, 0, ::7] = sc[1, 0, 3]  # exact ties in a continuous spread
+    print(f"[gpu] topk n={n} k={k}", flush=True)
+    _topk_case((n * 16, n * 16 - 9), n, k, 1, 1, 16, sc)
+
+
+def test_topk_all_equal_and_sals_units():
+    n = 1000
+    sc = np.full((1, 1, n), 2.5, dtype=np.float32)
+    _topk_case((n * 16,), n, 100, 1, 1, 16, sc)
+    rng = np.random.default_rng(3)
+    sc = rng.standard_normal((3, 1, 300)).astype(np.float32)
+    _topk_case((300 * 64, 299 * 64 + 5, 40 * 64), 300, 32, 0, 2, 64, sc)
+    _topk_case((300 * 64, 299 * 64 + 5, 40 * 64), 300, 10, 0, 0, 64, sc)
