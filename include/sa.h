@@ -113,10 +113,11 @@ const char *sa_status_string(int status);
 
 /*
  * Selection metadata buffers, sized for the whole cache.
- *  QUEST [Quest, min/max metadata]: meta = [num_pages, num_kv_heads, 2, head_dim]
- *        in the KV dtype; slot 0 = per-dimension max M, slot 1 = min m over the
- *        page's valid tokens.  Stored in the KV dtype (not fp16) so the values
- *        are exact and the bound stays valid.  meta_scale unused (NULL).
+ *  QUEST [Quest, min/max metadata]: meta = [num_kv_heads, num_pages, 2, head_dim]
+ *        in the KV dtype (head-major, so one kv-head's records of consecutive
+ *        physical pages are contiguous); slot 0 = per-dimension max M, slot 1 =
+ *        min m over the page's valid tokens.  Stored in the KV dtype (not fp16)
+ *        so the values are exact and the bound stays valid.  meta_scale unused.
  *  SALS  [SALS low-rank preprocessing; SeqO1 sketch K*P]: meta = int4 codes
  *        [num_pages, page_size, num_kv_heads, rank/2] bytes (two codes per
  *        byte, low nibble = even index, two's complement in [-7, 7]);
@@ -219,6 +220,12 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  * all of its units (k_compete + forced units >= sa_max_units) scoring is
  * skipped and dense attention runs.  sel / num_sel (optional, may be NULL)
  * receive the selection as sa_topk_pages writes it.
+ * Quest mode with one query head per kv-head runs as a single persistent
+ * kernel whose workgroups hand work to each other through control words at
+ * the head of the workspace: the workspace must be zero-filled before its
+ * first use, every call leaves those words zero again, and one workspace
+ * serves one call at a time.  A bounded wait that times out (never expected)
+ * sets the 32-bit word at byte offset 8 of the workspace to nonzero.
  */
 int sa_decode_step(const void *q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache *kv,
                    const sa_seqs *seqs, const sa_select_cfg *cfg, const void *meta,

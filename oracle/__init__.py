@@ -50,7 +50,7 @@ def _load():
     i, d, vp = ctypes.c_int, ctypes.c_double, ctypes.c_void_p
     lib.oracle_quest_meta.argtypes = [vp, i, i, i, i, i, vp, vp, i, i, vp]
     lib.oracle_quest_meta.restype = i
-    lib.oracle_quest_scores.argtypes = [vp, i, i, vp, i, i, i, i, vp, vp, i, i, vp, vp]
+    lib.oracle_quest_scores.argtypes = [vp, i, i, vp, i, i, i, i, i, vp, vp, i, i, vp, vp]
     lib.oracle_quest_scores.restype = None
     lib.oracle_sals_index.argtypes = [vp, i, vp, i, i, i, i, vp, vp, i, i, vp, i, vp, vp]
     lib.oracle_sals_index.restype = i
@@ -77,12 +77,13 @@ def _c(a, dtype=None):
 
 def quest_meta(k: np.ndarray, kv_dtype: str, page_table: np.ndarray, seq_lens: np.ndarray,
                meta: Optional[np.ndarray] = None) -> np.ndarray:
-    """Per (page, kv-head, dim) max (slot 0) and min (slot 1) over the page's valid tokens."""
+    """Per (kv-head, page, dim) max (slot 0) and min (slot 1) over the page's valid tokens;
+    layout [Hkv, P, 2, d]."""
     k = _c(k)
     P, S, Hkv, d = k.shape
     pt, sl = _c(page_table, np.int32), _c(seq_lens, np.int32)
     if meta is None:
-        meta = np.zeros((P, Hkv, 2, d), dtype=k.dtype)
+        meta = np.zeros((Hkv, P, 2, d), dtype=k.dtype)
     rc = _load().oracle_quest_meta(_p(k), DTYPES[kv_dtype], P, S, Hkv, d, _p(pt), _p(sl), pt.shape[0],
                                    pt.shape[1], _p(meta))
     if rc != 0:
@@ -96,13 +97,13 @@ def quest_scores(q: np.ndarray, q_dtype: str, meta: np.ndarray, kv_dtype: str,
     absolute magnitude; pages past the sequence get -inf."""
     q, meta = _c(q), _c(meta)
     B, Hq, d = q.shape
-    Hkv = meta.shape[1]
+    Hkv, P = meta.shape[0], meta.shape[1]
     pt, sl = _c(page_table, np.int32), _c(seq_lens, np.int32)
     mp = pt.shape[1]
     sc = np.empty((B, Hkv, mp), dtype=np.float64)
     ab = np.empty((B, Hkv, mp), dtype=np.float64)
-    _load().oracle_quest_scores(_p(q), DTYPES[q_dtype], Hq, _p(meta), DTYPES[kv_dtype], Hkv, d, PAGE,
-                                _p(pt), _p(sl), B, mp, _p(sc), _p(ab))
+    _load().oracle_quest_scores(_p(q), DTYPES[q_dtype], Hq, _p(meta), DTYPES[kv_dtype], Hkv, P, d,
+                                PAGE, _p(pt), _p(sl), B, mp, _p(sc), _p(ab))
     return sc, ab
 
 

@@ -31,7 +31,7 @@
  *   q        [B, Hq, d]              fp32 or bf16 bits
  *   K, V     [P, S, Hkv, d]          fp32, bf16 bits, or int8 codes
  *   k_scale  [P, S, Hkv]             fp16 bits (int8 caches)
- *   meta     [P, Hkv, 2, d]          KV dtype; slot 0 = per-dim max M, slot 1 = min m
+ *   meta     [Hkv, P, 2, d]          KV dtype; slot 0 = per-dim max M, slot 1 = min m
  *   codes    [P, S, Hkv, rank/2]     int4 pairs, low nibble = even index
  *   scales   [P, S, Hkv]             fp16 bits
  *   page_tbl [B, max_pages]          physical page of logical page p
@@ -135,8 +135,8 @@ int oracle_quest_meta(const void *k, int dtype, int num_pages, int S, int hkv, i
             if (x < mn) { mn = x; at_mn = is; }
           }
           uint8_t *dst = (uint8_t *)meta;
-          size_t oM = (((size_t)pp * hkv + h) * 2 + 0) * d + i;
-          size_t om = (((size_t)pp * hkv + h) * 2 + 1) * d + i;
+          size_t oM = (((size_t)h * num_pages + pp) * 2 + 0) * d + i;
+          size_t om = (((size_t)h * num_pages + pp) * 2 + 1) * d + i;
           memcpy(dst + oM * es, (const uint8_t *)k + at_mx * es, es);
           memcpy(dst + om * es, (const uint8_t *)k + at_mn * es, es);
         }
@@ -158,8 +158,9 @@ int oracle_quest_meta(const void *k, int dtype, int num_pages, int S, int hkv, i
  * Pages p >= n_b get -inf.
  */
 void oracle_quest_scores(const void *q, int q_dtype, int hq, const void *meta, int dtype, int hkv,
-                         int d, int S, const int32_t *page_table, const int32_t *seq_lens, int B,
-                         int max_pages, double *scores, double *abs_scale) {
+                         int num_pages, int d, int S, const int32_t *page_table,
+                         const int32_t *seq_lens, int B, int max_pages, double *scores,
+                         double *abs_scale) {
   int G = hq / hkv;
   for (int b = 0; b < B; ++b) {
     int n = ceil_div(seq_lens[b], S);
@@ -178,8 +179,8 @@ void oracle_quest_scores(const void *q, int q_dtype, int hq, const void *meta, i
           double s = 0.0, a = 0.0;
           for (int i = 0; i < d; ++i) {
             double qi = q_value(q, q_dtype, qo + i);
-            double Mi = kv_value(meta, dtype, (((size_t)pp * hkv + h) * 2 + 0) * d + i, NULL, 0);
-            double mi = kv_value(meta, dtype, (((size_t)pp * hkv + h) * 2 + 1) * d + i, NULL, 0);
+            double Mi = kv_value(meta, dtype, (((size_t)h * num_pages + pp) * 2 + 0) * d + i, NULL, 0);
+            double mi = kv_value(meta, dtype, (((size_t)h * num_pages + pp) * 2 + 1) * d + i, NULL, 0);
             double u1 = qi * mi, u2 = qi * Mi;
             s += u1 > u2 ? u1 : u2;
             a += fabs(qi) * (fabs(Mi) > fabs(mi) ? fabs(Mi) : fabs(mi));

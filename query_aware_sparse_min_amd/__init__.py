@@ -200,13 +200,19 @@ def alloc_meta(kv: KVCache, cfg: SelectCfg):
     dev = kv.k.device
     P, S, Hkv, d = kv.k.shape
     if cfg.mode == SA_MODE_QUEST:
-        return torch.empty((P, Hkv, 2, d), dtype=kv.k.dtype, device=dev), None
+        return torch.empty((Hkv, P, 2, d), dtype=kv.k.dtype, device=dev), None
     return (torch.empty((P, S, Hkv, cfg.rank // 2), dtype=torch.uint8, device=dev),
             torch.empty((P, S, Hkv), dtype=torch.int16, device=dev))
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
-    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+    """Zero-filled device workspace (sa_decode_step needs zeroed control words on first use)."""
+    return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def step_error_flag(workspace: torch.Tensor) -> int:
+    """The fused step's timeout flag (third 32-bit word of the workspace); 0 when healthy."""
+    return int(workspace[8:12].view(torch.int32).item())
 
 
 # ---------------------------------------------------------------- entry points

@@ -4,7 +4,10 @@
 // allocates, frees or synchronises.
 #include <string.h>
 
+#include <atomic>
+
 #include "sa_internal.h"
+#include "sa_step.h"
 
 using namespace sa;
 
@@ -92,22 +95,62 @@ Shapes shapes_of(int hq, const sa_kv_cache* kv, const sa_seqs* s) {
   return Shapes{s->batch, hq, kv->num_kv_heads, s->max_pages, kv->num_pages};
 }
 
+// Compute units of the current device (cached per device id).
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  if (dev < 64) {
+    const int c = cache[dev].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n < 1)
+    n = 256;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+// Co-resident workgroups of the fused step kernel on the current device,
+// cached per (device, kv dtype, q dtype).
+int resident_step_wgs(int kv_dtype, int q_dtype) {
+  static std::atomic<int> cache[64][4];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
+  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1);
+  if (dev < 64) {
+    const int c = cache[dev][slot].load(std::memory_order_relaxed);
+    if (c > 0) return c;
+  }
+  const int n = step_resident_wgs(kv_dtype, q_dtype, device_cus());
+  if (dev < 64 && n > 0) cache[dev][slot].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+constexpr int kPlanCUs = 256;  // task decomposition is planned for a 256-CU MI355X
+
 struct StepLayout {
-  size_t scores, sel, num_sel, partials, total;
+  size_t ctl, scores, sel, num_sel, partials, total;
   int max_units, max_sel;
-  bool dense;
+  bool dense;  // every list keeps all of its units: no scoring needed
+  bool fused;  // Quest: one persistent kernel for the whole step
   AttnPlan plan;
+  StepPlan splan;
 };
 
 StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa_select_cfg* c) {
   StepLayout L{};
   L.max_units = max_units_of(s, c);
   L.max_sel = max_sel_of(s, c);
-  // every list keeps all of its units: no scoring needed
   L.dense = (long long)c->k_compete + c->n_head_forced + c->n_tail_forced >= L.max_units;
+  L.fused = !L.dense && c->mode == SA_MODE_QUEST && hq / kv->num_kv_heads <= kStepMaxGroup;
   const size_t lists = (size_t)s->batch * kv->num_kv_heads;
   L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel);
+  L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
+  const size_t fused_part = (size_t)L.splan.lists * L.splan.ns * (hq / kv->num_kv_heads) * (kHeadDim + 2);
   size_t off = 0;
+  L.ctl = off;
+  off = align_up(off + step_ctl_bytes((int)lists));
   L.scores = off;
   off = align_up(off + (L.dense ? 0 : lists * L.max_units * sizeof(float)));
   L.sel = off;
@@ -115,7 +158,8 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   L.num_sel = off;
   off = align_up(off + lists * sizeof(int32_t));
   L.partials = off;
-  off = align_up(off + L.plan.partial_floats * sizeof(float));
+  const size_t pf = L.plan.partial_floats > fused_part ? L.plan.partial_floats : fused_part;
+  off = align_up(off + pf * sizeof(float));
   L.total = off;
   return L;
 }
@@ -284,6 +328,37 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
                                        nullptr, 0, lay.plan, softmax_scale, partials, out, st));
   }
   float* scores = reinterpret_cast<float*>(ws + lay.scores);
+  if (lay.fused) {
+    StepArgs A{};
+    A.q = q;
+    A.k = kv->k;
+    A.v = kv->v;
+    A.meta = meta;
+    A.pt = seqs->page_table;
+    A.lens = seqs->seq_lens;
+    A.B = seqs->batch;
+    A.hq = num_q_heads;
+    A.hkv = kv->num_kv_heads;
+    A.num_pages = kv->num_pages;
+    A.max_pages = seqs->max_pages;
+    A.k_compete = cfg->k_compete;
+    A.n_head = cfg->n_head_forced;
+    A.n_tail = cfg->n_tail_forced;
+    A.scale_log2 = softmax_scale * 1.4426950408889634f;
+    A.scores = scores;
+    A.sel = sel_buf;
+    A.num_sel = num_buf;
+    A.max_sel = lay.max_sel;
+    A.partials = partials;
+    A.out = out;
+    A.ctl = reinterpret_cast<StepCtl*>(ws + lay.ctl);
+    A.lctl = reinterpret_cast<ListCtl*>(ws + lay.ctl + sizeof(StepCtl));
+    StepPlan P = lay.splan;
+    int wgs = resident_step_wgs(kv->dtype, q_dtype);
+    if (wgs < 1) wgs = device_cus();  // one workgroup per CU always fits
+    P.grid = P.n_tasks < wgs ? P.n_tasks : wgs;
+    return hip_status(launch_quest_step(kv->dtype, q_dtype, A, P, st));
+  }
   if (cfg->mode == SA_MODE_QUEST)
     rc = hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
                                        seqs->seq_lens, scores, st));

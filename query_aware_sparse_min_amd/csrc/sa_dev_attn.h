@@ -1,0 +1,316 @@
+// sa_dev_attn.h - flash-decoding attention of one (batch, kv-head) list over
+// a range of its selected pages, inside one 256-thread workgroup, and the
+// merge of the per-split partials (device code shared by the standalone
+// attention kernel and the fused decode-step kernel).
+//
+// "Quest 完全拆解": approximate attention loads only the top-K pages through the
+// page table.  "SALS长序列推理优化", SFAA: QK -> online softmax -> P@V -> rescale on
+// int8 K/V gathered by the selection, rows split over cores then reduced.
+// "Day 10·2": the softmax is renormalised over the selected set only.
+//
+// Layout of the work: the four waves take the pages of the range in turn,
+// PW at a time so that 8 * PW row loads per lane are in flight.  Lane l owns token
+// row (l / 16) of a 4-row group and dimensions 8*(l % 16)..+7, so one 64-lane
+// load reads four whole rows of a page.  Scores are kept in base 2
+// (z = q.k * scale * log2 e); each wave keeps (max, sum, acc) per query head;
+// the workgroup folds its waves through LDS into one partial record
+// {acc[128], max, sum} per query head.
+#pragma once
+
+#include "sa_internal.h"
+
+namespace sa {
+
+constexpr int kPartStride = kHeadDim + 2;  // acc[d], max (base 2), sum
+
+template <int G>
+struct AttnSmem {
+  float acc[4][G][kHeadDim];
+  float m[4][G], l[4][G];
+};
+
+// 8 elements of a K/V row as raw words (widened when used).
+template <int DT>
+struct Raw8;
+template <>
+struct Raw8<SA_BF16> {
+  uint4 w;
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+    w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = bf16_lo(w.x); x[1] = bf16_hi(w.x); x[2] = bf16_lo(w.y); x[3] = bf16_hi(w.y);
+    x[4] = bf16_lo(w.z); x[5] = bf16_hi(w.z); x[6] = bf16_lo(w.w); x[7] = bf16_hi(w.w);
+  }
+};
+template <>
+struct Raw8<SA_F32> {
+  float4 a, b;
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+    const float4* p = reinterpret_cast<const float4*>(static_cast<const float*>(base) + e);
+    a = p[0];
+    b = p[1];
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+    x[0] = a.x; x[1] = a.y; x[2] = a.z; x[3] = a.w; x[4] = b.x; x[5] = b.y; x[6] = b.z; x[7] = b.w;
+  }
+};
+template <>
+struct Raw8<SA_I8> {
+  uint2 w;
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+    w = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(base) + e);
+  }
+  __device__ __forceinline__ void get(float (&x)[8]) const {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      x[i] = (float)(int8_t)(w.x >> (8 * i));
+      x[4 + i] = (float)(int8_t)(w.y >> (8 * i));
+    }
+  }
+};
+
+struct PageRef {
+  int pp;  // physical page, -1 if the slot is empty
+  int nv;  // valid tokens
+};
+
+// Attend to pages lst[j0 .. j1) (lst == nullptr: logical pages j0 .. j1) of
+// list (b, h) and write the workgroup's partial records to part[G][kPartStride].
+// PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
+// COH: the page list is read and the partials are written device-coherently.
+template <int KT, int QT, int G, int PW = 2, bool COH = false>
+__device__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
+                             const void* __restrict__ v, const uint16_t* __restrict__ ks,
+                             const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
+                             const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
+                             int j1, float scale_log2, float* __restrict__ part,
+                             AttnSmem<G>& sm) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int hq = hkv * G;
+  const int np = (L + kPage - 1) / kPage;
+
+  float qv[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) load8<QT>(q, ((size_t)b * hq + (size_t)h * G + g) * kHeadDim + 8 * c, qv[g]);
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+  }
+
+  // Resolve this wave's pages j = j0 + wave + 4 * x (x < 64) up front: lane x
+  // loads list entry x, then its page-table entry, so the list and the page
+  // table cost one memory round trip each instead of one per page.
+  int my_pp = -1, my_nv = 0;
+  {
+    const int j = j0 + wave + 4 * lane;
+    int p = -1;
+    if (j < j1) p = lst ? ld_x<COH>(lst + j) : j;
+    if (p >= 0 && p < np) {
+      const int pp = pt_row[p];
+      if (pp >= 0 && pp < num_pages) {
+        my_pp = pp;
+        my_nv = min(kPage, L - p * kPage);
+      }
+    }
+  }
+  auto page_of = [&](int j) -> PageRef {
+    PageRef pr{-1, 0};
+    if (j >= j1) return pr;
+    const int x = (j - j0 - wave) >> 2;  // wave-uniform
+    if (x < 64) {
+      pr.pp = __shfl(my_pp, x, 64);
+      pr.nv = __shfl(my_nv, x, 64);
+      return pr;
+    }
+    const int p = lst ? ld_x<COH>(lst + j) : j;  // wave with more than 64 pages
+    if (p < 0 || p >= np) return pr;
+    const int pp = pt_row[p];
+    if (pp < 0 || pp >= num_pages) return pr;
+    pr.pp = pp;
+    pr.nv = min(kPage, L - p * kPage);
+    return pr;
+  };
+
+  for (int jb = j0 + wave; jb < j1; jb += 4 * PW) {
+    PageRef pg[PW];
+    Raw8<KT> kr[PW][4], vr[PW][4];
+    float ksc[PW][4], vsc[PW][4];
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      pg[u] = page_of(jb + 4 * u);
+      if (pg[u].pp >= 0) {
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          const size_t tok = ((size_t)pg[u].pp * kPage + 4 * it + r) * hkv + h;
+          kr[u][it].load(k, tok * kHeadDim + 8 * c);
+          vr[u][it].load(v, tok * kHeadDim + 8 * c);
+          if constexpr (KT == SA_I8) {
+            ksc[u][it] = f16_to_f32(ks[tok]);
+            vsc[u][it] = f16_to_f32(vs[tok]);
+          } else {
+            ksc[u][it] = vsc[u][it] = 1.0f;
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      if (pg[u].pp < 0) continue;  // wave-uniform
+#pragma unroll
+      for (int g = 0; g < G; ++g) {
+        float z[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          float kx[8];
+          kr[u][it].get(kx);
+          float s = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[e], s);
+          s = xor_sum<1>(s);
+          s = xor_sum<2>(s);
+          s = xor_sum<4>(s);
+          s = xor_sum<8>(s);
+          z[it] = (4 * it + r < pg[u].nv) ? s * (scale_log2 * ksc[u][it]) : -INFINITY;
+        }
+        float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
+        pm = xor_max<16>(pm);
+        pm = xor_max<32>(pm);
+        const float mn = fmaxf(m[g], pm);  // finite: slot 0 of a kept page is valid
+        const float alpha = exp2f(m[g] - mn);
+        float pr[4], psum = 0.0f;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          pr[it] = exp2f(z[it] - mn);
+          psum += pr[it];
+          pr[it] *= vsc[u][it];
+        }
+        l[g] = l[g] * alpha + psum;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= alpha;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          float vx[8];
+          vr[u][it].get(vx);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pr[it], vx[e], acc[g][e]);
+        }
+        m[g] = mn;
+      }
+    }
+  }
+
+  // fold the four token rows of each wave, then the four waves
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    l[g] = xor_sum<32>(xor_sum<16>(l[g]));
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = xor_sum<32>(xor_sum<16>(acc[g][e]));
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.acc[wave][g][8 * c + e] = acc[g][e];
+      if (c == 0) {
+        sm.m[wave][g] = m[g];
+        sm.l[wave][g] = l[g];
+      }
+    }
+  }
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += blockDim.x) {
+    const int g = idx / kHeadDim, dim = idx % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][g]);
+    float a = 0.0f, ls = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < 4; ++w) {
+        const float f = exp2f(sm.m[w][g] - M);
+        a = fmaf(sm.acc[w][g][dim], f, a);
+        ls = fmaf(sm.l[w][g], f, ls);
+      }
+    }
+    st_x<COH>(part + g * kPartStride + dim, a);
+    if (dim == 0) {
+      st_x<COH>(part + g * kPartStride + kHeadDim, M);
+      st_x<COH>(part + g * kPartStride + kHeadDim + 1, ls);
+    }
+  }
+}
+
+struct MergeSmem {
+  float w[2048];  // per (split, head) weight 2^(m_s - M)
+  float M[16];
+};
+
+// Merge ns partial records part[ns][G][kPartStride] of one list into
+// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Requires ns * G <= 2048.  COH: partials are read device-coherently.  All
+// threads of the workgroup call.
+template <bool COH = false>
+__device__ __forceinline__ void merge_list(const float* __restrict__ part, int ns, int G,
+                                           float* __restrict__ out, MergeSmem& sm) {
+  const int tid = threadIdx.x, nt = blockDim.x;
+  const int tot = ns * G;
+  // (max, sum) of every record: up to 8 loads in flight per thread
+  for (int i0 = 0; i0 < tot; i0 += 8 * nt) {
+    float ls[8], ms[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + tid + j * nt;
+      ls[j] = i < tot ? ld_x<COH>(part + (size_t)i * kPartStride + kHeadDim + 1) : 0.0f;
+      ms[j] = i < tot ? ld_x<COH>(part + (size_t)i * kPartStride + kHeadDim) : 0.0f;
+    }
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int i = i0 + tid + j * nt;
+      if (i < tot) sm.w[i] = ls[j] > 0.0f ? ms[j] : -INFINITY;
+    }
+  }
+  __syncthreads();
+  if (tid < G) {
+    float M = -INFINITY;
+    for (int s = 0; s < ns; ++s) M = fmaxf(M, sm.w[s * G + tid]);
+    sm.M[tid] = M;
+  }
+  __syncthreads();
+  for (int i = tid; i < tot; i += nt) {
+    const float M = sm.M[i % G];
+    sm.w[i] = (sm.w[i] == -INFINITY) ? 0.0f : exp2f(sm.w[i] - M);
+  }
+  __syncthreads();
+  for (int o = tid; o < G * kHeadDim; o += nt) {
+    const int g = o / kHeadDim, dim = o % kHeadDim;
+    float a = 0.0f, lsum = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += 8) {  // 8 independent record loads in flight
+      float av[8], lv[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = s0 + j;
+        const float* rec = part + ((size_t)s * G + g) * kPartStride;
+        const bool use = s < ns && sm.w[(s < ns ? s : 0) * G + g] > 0.0f;
+        av[j] = use ? ld_x<COH>(rec + dim) : 0.0f;
+        lv[j] = use ? ld_x<COH>(rec + kHeadDim + 1) : 0.0f;
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int s = s0 + j;
+        const float w = s < ns ? sm.w[s * G + g] : 0.0f;
+        a = fmaf(av[j], w, a);
+        lsum = fmaf(lv[j], w, lsum);
+      }
+    }
+    out[o] = lsum > 0.0f ? a / lsum : 0.0f;
+  }
+}
+
+}  // namespace sa

@@ -61,6 +61,30 @@ __device__ __forceinline__ float xor_max(float v) {
   return fmaxf(v, __shfl_xor(v, MASK, 64));
 }
 
+// ------------------------------------------- cross-workgroup hand-off memory
+// Data that one workgroup of a kernel writes and another reads in the same
+// launch goes through device-coherent (sc1) stores and loads: the 8 XCD L2
+// caches are not coherent with each other, and these accesses bypass stale
+// copies without the whole-cache write-back / invalidate of an agent-scope
+// fence.  COH = false gives plain accesses (hand-off across kernel launches).
+template <bool COH, typename T>
+__device__ __forceinline__ T ld_x(const T* p) {
+  if constexpr (COH) return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else return *p;
+}
+template <bool COH, typename T>
+__device__ __forceinline__ void st_x(T* p, T v) {
+  if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  else *p = v;
+}
+// Wait until this thread's stores have completed (s_waitcnt vmcnt(0)); the
+// signal fences keep the compiler from moving memory accesses across it.
+__device__ __forceinline__ void stores_done() {
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+  __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0), expcnt/lgkmcnt untouched
+  __atomic_signal_fence(__ATOMIC_SEQ_CST);
+}
+
 // ------------------------------------------------------------ launchers
 // Every launcher enqueues on 'stream' and returns hipGetLastError() of the launch.
 struct Shapes {

@@ -89,8 +89,9 @@ __global__ __launch_bounds__(256) void quest_meta_kernel(const void* __restrict_
         if (x < fmn[e]) { fmn[e] = x; mn.set(e, v.bits(e)); }
       }
     }
-    mx.store(meta + ((((size_t)pp * hkv + h) * 2 + 0) * kHeadDim + i0) * ES);
-    mn.store(meta + ((((size_t)pp * hkv + h) * 2 + 1) * kHeadDim + i0) * ES);
+    // head-major [Hkv][num_pages][2][d]: one list's records are contiguous
+    mx.store(meta + ((((size_t)h * num_pages + pp) * 2 + 0) * kHeadDim + i0) * ES);
+    mn.store(meta + ((((size_t)h * num_pages + pp) * 2 + 1) * kHeadDim + i0) * ES);
   }
 }
 

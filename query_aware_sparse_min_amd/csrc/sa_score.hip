@@ -11,12 +11,13 @@
 //    group mean of q projected by P; per token s_t = scale_t * qt . c_t from
 //    the int4 codes; per block a log-sum-exp of tau * s_t, kept as an online
 //    (max, sum) pair in base 2 and merged across the lanes of a kv-head.
-#include "sa_internal.h"
+#include "sa_dev_score.h"
 
 namespace sa {
 namespace {
 
-constexpr int kScorePagesPerWG = 32;  // 4 waves x 4 iterations x 2 pages
+constexpr int kScoreIT = 4;                        // loads per lane
+constexpr int kScorePagesPerWG = 8 * kScoreIT;      // 32 pages per workgroup
 
 // grid (ceil(max_pages / 32), Hkv, B), block 256
 template <int KT, int QT, int G>
@@ -27,61 +28,11 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   const int h = blockIdx.y, b = blockIdx.z;
   const int L = clamp_len(lens[b], max_pages);
   const int n = (L + kPage - 1) / kPage;
-  const int p_base = blockIdx.x * kScorePagesPerWG;
-  if (p_base >= n) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int half = lane >> 5, row = (lane >> 4) & 1, c = lane & 15;
-  const int hq = hkv * G;
-
-  float qs[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    float x[8];
-    load8<QT>(q, ((size_t)b * hq + (size_t)h * G + g) * kHeadDim + 8 * c, x);
-#pragma unroll
-    for (int e = 0; e < 8; ++e) qs[g][e] = row ? fminf(x[e], 0.0f) : fmaxf(x[e], 0.0f);
-  }
-
-  float x[4][8];
-  int pg[4];
-  bool ok[4];
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    const int p = p_base + wave * 8 + it * 2 + half;
-    int pp = 0;
-    bool v = p < n;
-    if (v) {
-      pp = pt[(size_t)b * max_pages + p];
-      v = pp >= 0 && pp < num_pages;
-    }
-    pg[it] = p;
-    ok[it] = v;
-    if (v) {
-      load8<KT>(meta, (((size_t)pp * hkv + h) * 2 + row) * kHeadDim + 8 * c, x[it]);
-    } else {
-#pragma unroll
-      for (int e = 0; e < 8; ++e) x[it][e] = 0.0f;
-    }
-  }
-#pragma unroll
-  for (int it = 0; it < 4; ++it) {
-    float best = -INFINITY;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float s = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) s = fmaf(qs[g][e], x[it][e], s);
-      s = xor_sum<1>(s);
-      s = xor_sum<2>(s);
-      s = xor_sum<4>(s);
-      s = xor_sum<8>(s);
-      s = xor_sum<16>(s);
-      best = fmaxf(best, s);
-    }
-    const int p = pg[it];
-    if ((lane & 31) == 0 && p < n)
-      scores[((size_t)b * hkv + h) * max_pages + p] = ok[it] ? best : -INFINITY;
-  }
+  const int p0 = blockIdx.x * kScorePagesPerWG;
+  if (p0 >= n) return;
+  quest_score_range<KT, QT, G, kScoreIT>(q, meta, num_pages, hkv, b, h, pt + (size_t)b * max_pages,
+                                         p0, min(p0 + kScorePagesPerWG, n),
+                                         scores + ((size_t)b * hkv + h) * max_pages);
 }
 
 // grid (ceil(max_units / units_per_wg), B), block 256

@@ -1,0 +1,62 @@
+// sa_step.h - plan, control words and launcher of the fused decode-step kernel.
+#pragma once
+
+#include "sa_internal.h"
+
+namespace sa {
+
+// Query heads per kv-head the fused kernel is built for (larger groups run
+// the separate scorer / top-K / attention kernels).
+constexpr int kStepMaxGroup = 1;
+
+// Control words at the head of the step workspace.
+struct StepCtl {
+  uint32_t reserved[2];
+  uint32_t error;  // nonzero after a bounded wait timed out
+  uint32_t pad[13];
+};
+struct ListCtl {  // one 64-byte record per (batch, kv-head) list
+  uint32_t score_done;
+  uint32_t sel_ready;
+  uint32_t attn_done;
+  uint32_t pad[13];
+};
+
+struct StepPlan {
+  int lists;        // B * Hkv
+  int chunk_pages;  // pages per score task
+  int nc;           // score tasks per list
+  int pps;          // selected pages per attention task
+  int ns;           // attention tasks per list
+  int n_tasks;
+  int grid;         // workgroups launched: all must be co-resident
+};
+
+struct StepArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* meta;
+  const int32_t* pt;
+  const int32_t* lens;
+  int B, hq, hkv, num_pages, max_pages;
+  int k_compete, n_head, n_tail;
+  float scale_log2;
+  float* scores;    // [lists][max_pages]
+  int32_t* sel;     // [lists][max_sel]
+  int32_t* num_sel; // [lists]
+  int max_sel;
+  float* partials;  // [lists][ns][G][kHeadDim + 2]
+  float* out;       // [B][hq][kHeadDim]
+  StepCtl* ctl;
+  ListCtl* lctl;
+};
+
+StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_cus);
+// Workgroups of the fused kernel that fit on the device at once (0 on error).
+int step_resident_wgs(int kv_dtype, int q_dtype, int num_cus);
+size_t step_ctl_bytes(int lists);
+hipError_t launch_quest_step(int kv_dtype, int q_dtype, const StepArgs& A, const StepPlan& P,
+                             hipStream_t st);
+
+}  // namespace sa

@@ -84,6 +84,7 @@ class GpuCase:
             num = torch.full((wl.B, wl.Hkv), -7, dtype=torch.int32, device=self.dev)
         sa.sa_decode_step(self.q(q_np), self.kv, self.seqs, self.cfg, self.meta, self.meta_scale,
                           wl.softmax_scale, out, ws, sel, num)
+        assert sa.step_error_flag(ws) == 0, "a bounded wait of the fused step timed out"
         return out, sel, num
 
 

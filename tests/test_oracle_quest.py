@@ -43,11 +43,11 @@ def test_meta_is_bruteforce_min_max(case):
         for p in range(wl.n_pages(b)):
             pp, nv = _tokens(wl, b, p)
             keys = K[pp, :nv]  # [nv, Hkv, d]
-            assert np.array_equal(M[pp, :, 0], keys.max(axis=0))
-            assert np.array_equal(M[pp, :, 1], keys.min(axis=0))
+            assert np.array_equal(M[:, pp, 0], keys.max(axis=0))
+            assert np.array_equal(M[:, pp, 1], keys.min(axis=0))
             # every bound value is attained by a valid token of the page
-            assert np.all((keys == M[pp, :, 0][None]).any(axis=0))
-            assert np.all((keys == M[pp, :, 1][None]).any(axis=0))
+            assert np.all((keys == M[:, pp, 0][None]).any(axis=0))
+            assert np.all((keys == M[:, pp, 1][None]).any(axis=0))
 
 
 def test_meta_matches_incremental_update():
@@ -63,8 +63,8 @@ def test_meta_matches_incremental_update():
         for s in range(nv):
             Mx = np.maximum(Mx, K[pp, s])
             mn = np.minimum(mn, K[pp, s])
-        assert np.array_equal(_kv_f64(wl, meta[pp, :, 0]), Mx)
-        assert np.array_equal(_kv_f64(wl, meta[pp, :, 1]), mn)
+        assert np.array_equal(_kv_f64(wl, meta[:, pp, 0]), Mx)
+        assert np.array_equal(_kv_f64(wl, meta[:, pp, 1]), mn)
 
 
 @pytest.mark.parametrize("case", CASES)
@@ -101,7 +101,7 @@ def test_bound_equals_linear_form(case):
             pp = int(wl.page_table[b, p])
             for h in range(wl.Hkv):
                 qg = Q[b, h * G:(h + 1) * G]
-                lin = np.maximum(qg, 0) @ Mt[pp, h, 0] + np.minimum(qg, 0) @ Mt[pp, h, 1]
+                lin = np.maximum(qg, 0) @ Mt[h, pp, 0] + np.minimum(qg, 0) @ Mt[h, pp, 1]
                 assert abs(sc[b, h, p] - lin.max()) <= 1e-12 * ab[b, h, p]
 
 
@@ -117,7 +117,7 @@ def test_one_hot_query_reads_one_bound():
             for p in range(wl.n_pages(0)):
                 pp = int(wl.page_table[0, p])
                 for h in range(2):
-                    want = meta[pp, h, 0, i] if sign > 0 else -meta[pp, h, 1, i]
+                    want = meta[h, pp, 0, i] if sign > 0 else -meta[h, pp, 1, i]
                     assert sc[0, h, p] == want
 
 
