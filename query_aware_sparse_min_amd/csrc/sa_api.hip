@@ -113,16 +113,17 @@ int device_cus() {
 
 // Co-resident workgroups of the fused step kernel on the current device,
 // cached per (device, kv dtype, q dtype).
-int resident_step_wgs(int kv_dtype, int q_dtype) {
-  static std::atomic<int> cache[64][4];
+int resident_step_wgs(int kv_dtype, int q_dtype, int max_pages) {
+  static std::atomic<int> cache[64][8];
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
-  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1);
+  const int kpt = step_kpt(max_pages);
+  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1) + (kpt > 8 ? 4 : 0);
   if (dev < 64) {
     const int c = cache[dev][slot].load(std::memory_order_relaxed);
     if (c > 0) return c;
   }
-  const int n = step_resident_wgs(kv_dtype, q_dtype, device_cus());
+  const int n = step_resident_wgs(kv_dtype, q_dtype, kpt, device_cus());
   if (dev < 64 && n > 0) cache[dev][slot].store(n, std::memory_order_relaxed);
   return n;
 }
@@ -130,7 +131,7 @@ int resident_step_wgs(int kv_dtype, int q_dtype) {
 constexpr int kPlanCUs = 256;  // task decomposition is planned for a 256-CU MI355X
 
 struct StepLayout {
-  size_t ctl, scores, sel, num_sel, partials, total;
+  size_t ctl, scores, sel, num_sel, rsel, partials, total;
   int max_units, max_sel;
   bool dense;  // every list keeps all of its units: no scoring needed
   bool fused;  // Quest: one persistent kernel for the whole step
@@ -143,7 +144,8 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   L.max_units = max_units_of(s, c);
   L.max_sel = max_sel_of(s, c);
   L.dense = (long long)c->k_compete + c->n_head_forced + c->n_tail_forced >= L.max_units;
-  L.fused = !L.dense && c->mode == SA_MODE_QUEST && hq / kv->num_kv_heads <= kStepMaxGroup;
+  L.fused = !L.dense && c->mode == SA_MODE_QUEST && hq / kv->num_kv_heads <= kStepMaxGroup &&
+            s->max_pages <= kStepMaxPages && kv->num_pages <= kStepMaxPhysPages;
   const size_t lists = (size_t)s->batch * kv->num_kv_heads;
   L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel);
   L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
@@ -157,6 +159,8 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   off = align_up(off + lists * L.max_sel * sizeof(int32_t));
   L.num_sel = off;
   off = align_up(off + lists * sizeof(int32_t));
+  L.rsel = off;
+  off = align_up(off + (L.fused ? lists * L.max_sel * sizeof(int32_t) : 0));
   L.partials = off;
   const size_t pf = L.plan.partial_floats > fused_part ? L.plan.partial_floats : fused_part;
   off = align_up(off + pf * sizeof(float));
@@ -348,13 +352,14 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
     A.scores = scores;
     A.sel = sel_buf;
     A.num_sel = num_buf;
+    A.rsel = reinterpret_cast<int32_t*>(ws + lay.rsel);
     A.max_sel = lay.max_sel;
     A.partials = partials;
     A.out = out;
     A.ctl = reinterpret_cast<StepCtl*>(ws + lay.ctl);
     A.lctl = reinterpret_cast<ListCtl*>(ws + lay.ctl + sizeof(StepCtl));
     StepPlan P = lay.splan;
-    int wgs = resident_step_wgs(kv->dtype, q_dtype);
+    int wgs = resident_step_wgs(kv->dtype, q_dtype, seqs->max_pages);
     if (wgs < 1) wgs = device_cus();  // one workgroup per CU always fits
     P.grid = P.n_tasks < wgs ? P.n_tasks : wgs;
     return hip_status(launch_quest_step(kv->dtype, q_dtype, A, P, st));

@@ -36,11 +36,10 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 __global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __restrict__ partials,
                                                             int hkv, int G, int nsplit,
                                                             float* __restrict__ out) {
-  __shared__ MergeSmem sm;
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t list = (size_t)b * hkv + h;
   merge_list(partials + list * nsplit * G * kPartStride, nsplit, G,
-             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, sm);
+             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim);
 }
 
 template <int KT, int QT>
@@ -68,7 +67,7 @@ hipError_t attn_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, cons
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len) {
   // Enough workgroups to cover the 256 CUs several times over; at least one
-  // page per wave of a split; the merge keeps one weight per (split, head).
+  // page per wave of a split.
   constexpr long kTargetWGs = 2048;
   AttnPlan p{};
   p.list_len = list_len < 1 ? 1 : list_len;
@@ -76,8 +75,6 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len) {
   const int G = Hq / Hkv;
   long pps = (lists * p.list_len + kTargetWGs - 1) / kTargetWGs;
   if (pps < 4) pps = 4;
-  const long min_pps = ((long)p.list_len * G + 2047) / 2048;
-  if (pps < min_pps) pps = min_pps;
   p.pps = (int)pps;
   p.nsplit = (p.list_len + p.pps - 1) / p.pps;
   p.partial_floats = (size_t)lists * p.nsplit * G * kPartStride;

@@ -77,15 +77,17 @@ struct PageRef {
 
 // Attend to pages lst[j0 .. j1) (lst == nullptr: logical pages j0 .. j1) of
 // list (b, h) and write the workgroup's partial records to part[G][kPartStride].
+// rlst (optional) holds the same pages already resolved to
+// (physical page << 4) | (valid tokens - 1); the page table is then not read.
 // PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
 // COH: the page list is read and the partials are written device-coherently.
 template <int KT, int QT, int G, int PW = 2, bool COH = false>
-__device__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
+__device__ __forceinline__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
                              const void* __restrict__ v, const uint16_t* __restrict__ ks,
                              const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
                              const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
                              int j1, float scale_log2, float* __restrict__ part,
-                             AttnSmem<G>& sm) {
+                             AttnSmem<G>& sm, const int32_t* rlst = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int hq = hkv * G;
@@ -108,7 +110,14 @@ __device__ void attend_range(const void* __restrict__ q, const void* __restrict_
   // loads list entry x, then its page-table entry, so the list and the page
   // table cost one memory round trip each instead of one per page.
   int my_pp = -1, my_nv = 0;
-  {
+  if (rlst) {
+    const int j = j0 + wave + 4 * lane;
+    const int32_t r = j < j1 ? ld_x<COH>(rlst + j) : -1;
+    if (r >= 0) {
+      my_pp = r >> 4;
+      my_nv = (r & 15) + 1;
+    }
+  } else {
     const int j = j0 + wave + 4 * lane;
     int p = -1;
     if (j < j1) p = lst ? ld_x<COH>(lst + j) : j;
@@ -129,7 +138,15 @@ __device__ void attend_range(const void* __restrict__ q, const void* __restrict_
       pr.nv = __shfl(my_nv, x, 64);
       return pr;
     }
-    const int p = lst ? ld_x<COH>(lst + j) : j;  // wave with more than 64 pages
+    if (rlst) {  // wave with more than 64 pages
+      const int32_t r = ld_x<COH>(rlst + j);
+      if (r >= 0) {
+        pr.pp = r >> 4;
+        pr.nv = (r & 15) + 1;
+      }
+      return pr;
+    }
+    const int p = lst ? ld_x<COH>(lst + j) : j;
     if (p < 0 || p >= np) return pr;
     const int pp = pt_row[p];
     if (pp < 0 || pp >= num_pages) return pr;
@@ -145,18 +162,17 @@ __device__ void attend_range(const void* __restrict__ q, const void* __restrict_
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       pg[u] = page_of(jb + 4 * u);
-      if (pg[u].pp >= 0) {
+      const int ppl = pg[u].pp >= 0 ? pg[u].pp : 0;  // empty slot: load page 0, result unused
 #pragma unroll
-        for (int it = 0; it < 4; ++it) {
-          const size_t tok = ((size_t)pg[u].pp * kPage + 4 * it + r) * hkv + h;
-          kr[u][it].load(k, tok * kHeadDim + 8 * c);
-          vr[u][it].load(v, tok * kHeadDim + 8 * c);
-          if constexpr (KT == SA_I8) {
-            ksc[u][it] = f16_to_f32(ks[tok]);
-            vsc[u][it] = f16_to_f32(vs[tok]);
-          } else {
-            ksc[u][it] = vsc[u][it] = 1.0f;
-          }
+      for (int it = 0; it < 4; ++it) {
+        const size_t tok = ((size_t)ppl * kPage + 4 * it + r) * hkv + h;
+        kr[u][it].load(k, tok * kHeadDim + 8 * c);
+        vr[u][it].load(v, tok * kHeadDim + 8 * c);
+        if constexpr (KT == SA_I8) {
+          ksc[u][it] = f16_to_f32(ks[tok]);
+          vsc[u][it] = f16_to_f32(vs[tok]);
+        } else {
+          ksc[u][it] = vsc[u][it] = 1.0f;
         }
       }
     }
@@ -247,67 +263,47 @@ __device__ void attend_range(const void* __restrict__ q, const void* __restrict_
   }
 }
 
-struct MergeSmem {
-  float w[2048];  // per (split, head) weight 2^(m_s - M)
-  float M[16];
-};
-
 // Merge ns partial records part[ns][G][kPartStride] of one list into
-// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// Requires ns * G <= 2048.  COH: partials are read device-coherently.  All
-// threads of the workgroup call.
+// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Each
+// output element fetches the (acc, max, sum) of 16 splits at a time and folds
+// them into a running (M, acc, sum), so 16 splits cost one memory round trip.
+// COH: partials are read device-coherently.  All threads of the workgroup call.
 template <bool COH = false>
 __device__ __forceinline__ void merge_list(const float* __restrict__ part, int ns, int G,
-                                           float* __restrict__ out, MergeSmem& sm) {
-  const int tid = threadIdx.x, nt = blockDim.x;
-  const int tot = ns * G;
-  // (max, sum) of every record: up to 8 loads in flight per thread
-  for (int i0 = 0; i0 < tot; i0 += 8 * nt) {
-    float ls[8], ms[8];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + tid + j * nt;
-      ls[j] = i < tot ? ld_x<COH>(part + (size_t)i * kPartStride + kHeadDim + 1) : 0.0f;
-      ms[j] = i < tot ? ld_x<COH>(part + (size_t)i * kPartStride + kHeadDim) : 0.0f;
-    }
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int i = i0 + tid + j * nt;
-      if (i < tot) sm.w[i] = ls[j] > 0.0f ? ms[j] : -INFINITY;
-    }
-  }
-  __syncthreads();
-  if (tid < G) {
-    float M = -INFINITY;
-    for (int s = 0; s < ns; ++s) M = fmaxf(M, sm.w[s * G + tid]);
-    sm.M[tid] = M;
-  }
-  __syncthreads();
-  for (int i = tid; i < tot; i += nt) {
-    const float M = sm.M[i % G];
-    sm.w[i] = (sm.w[i] == -INFINITY) ? 0.0f : exp2f(sm.w[i] - M);
-  }
-  __syncthreads();
-  for (int o = tid; o < G * kHeadDim; o += nt) {
+                                           float* __restrict__ out) {
+  constexpr int C = 16;
+  for (int o = threadIdx.x; o < G * kHeadDim; o += blockDim.x) {
     const int g = o / kHeadDim, dim = o % kHeadDim;
-    float a = 0.0f, lsum = 0.0f;
-    for (int s0 = 0; s0 < ns; s0 += 8) {  // 8 independent record loads in flight
-      float av[8], lv[8];
+    float M = -INFINITY, a = 0.0f, lsum = 0.0f;
+    for (int s0 = 0; s0 < ns; s0 += C) {
+      float av[C], mv[C], lv[C];
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int s = s0 + j;
-        const float* rec = part + ((size_t)s * G + g) * kPartStride;
-        const bool use = s < ns && sm.w[(s < ns ? s : 0) * G + g] > 0.0f;
-        av[j] = use ? ld_x<COH>(rec + dim) : 0.0f;
-        lv[j] = use ? ld_x<COH>(rec + kHeadDim + 1) : 0.0f;
+      for (int j = 0; j < C; ++j) {  // unconditional loads (clamped split) stay in flight together
+        const float* rec = part + ((size_t)min(s0 + j, ns - 1) * G + g) * kPartStride;
+        av[j] = ld_x<COH>(rec + dim);
+        mv[j] = ld_x<COH>(rec + kHeadDim);
+        lv[j] = ld_x<COH>(rec + kHeadDim + 1);
       }
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const int s = s0 + j;
-        const float w = s < ns ? sm.w[s * G + g] : 0.0f;
-        a = fmaf(av[j], w, a);
-        lsum = fmaf(lv[j], w, lsum);
+      for (int j = 0; j < C; ++j)
+        if (s0 + j >= ns) lv[j] = 0.0f;
+      float Mc = M;
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+        if (lv[j] > 0.0f) Mc = fmaxf(Mc, mv[j]);
+      if (Mc == -INFINITY) continue;  // nothing attended so far
+      const float r = exp2f(M - Mc);  // 0 when M is still -inf
+      a *= r;
+      lsum *= r;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        if (lv[j] > 0.0f) {
+          const float w = exp2f(mv[j] - Mc);
+          a = fmaf(av[j], w, a);
+          lsum = fmaf(lv[j], w, lsum);
+        }
       }
+      M = Mc;
     }
     out[o] = lsum > 0.0f ? a / lsum : 0.0f;
   }

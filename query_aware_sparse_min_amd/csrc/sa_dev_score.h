@@ -28,19 +28,21 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
   const int half = lane >> 5, row = (lane >> 4) & 1, c = lane & 15;
   const int hq = hkv * G;
 
+  // all loads are unconditional, from clamped in-range addresses, so that they
+  // are in flight together; out-of-range results are discarded below
   int pg[IT];
   int ppg[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
     const int p = p0 + 2 * (wave + 4 * it) + half;
     pg[it] = p;
-    ppg[it] = p < p1 ? pt_row[p] : -1;
+    ppg[it] = pt_row[min(p, p1 - 1)];
   }
   Raw8<KT> x[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    if (ppg[it] >= 0 && ppg[it] < num_pages)
-      x[it].load(meta, (((size_t)h * num_pages + ppg[it]) * 2 + row) * kHeadDim + 8 * c);
+    const int pp = (ppg[it] >= 0 && ppg[it] < num_pages) ? ppg[it] : 0;
+    x[it].load(meta, (((size_t)h * num_pages + pp) * 2 + row) * kHeadDim + 8 * c);
   }
   float qs[G][8];
 #pragma unroll
@@ -52,7 +54,7 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const bool ok = ppg[it] >= 0 && ppg[it] < num_pages;
+    const bool ok = pg[it] < p1 && ppg[it] >= 0 && ppg[it] < num_pages;
     float xv[8];
     if (ok) {
       x[it].get(xv);

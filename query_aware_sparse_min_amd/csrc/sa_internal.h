@@ -52,6 +52,70 @@ __device__ __forceinline__ int clamp_len(int L, int max_pages) {
 }
 
 // --------------------------------------------------------- wave reductions
+// Cross-lane exchanges on the VALU (DPP row permutes and the gfx950
+// permlane16/32 swaps) rather than LDS-crossbar permutes.  Every step pairs
+// lanes symmetrically, so all lanes of a group end with bit-identical values.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return (uint32_t)__builtin_amdgcn_update_dpp((int)v, (int)v, CTRL, 0xF, 0xF, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f32(float v) {
+  return __uint_as_float(dpp_u32<CTRL>(__float_as_uint(v)));
+}
+constexpr int kDppXor1 = 0xB1;        // quad_perm [1,0,3,2]
+constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
+constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
+constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16 lanes
+
+// partner lane (l ^ 16) / (l ^ 32) values, exchanged in one VALU op
+__device__ __forceinline__ uint32_t swap16_u32(uint32_t v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  return r[0] == v ? r[1] : r[0];
+}
+__device__ __forceinline__ float sum16(float v) {  // all-reduce over each 16-lane row
+  v += dpp_f32<kDppXor1>(v);
+  v += dpp_f32<kDppXor2>(v);
+  v += dpp_f32<kDppHalfMirror>(v);
+  v += dpp_f32<kDppMirror>(v);
+  return v;
+}
+__device__ __forceinline__ float pair16_sum(float v) {  // + lane l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair32_sum(float v) {  // + lane l ^ 32
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float pair16_max(float v) {
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float pair32_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  v = min(v, dpp_u32<kDppXor1>(v));
+  v = min(v, dpp_u32<kDppXor2>(v));
+  v = min(v, dpp_u32<kDppHalfMirror>(v));
+  v = min(v, dpp_u32<kDppMirror>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = min(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return min(b[0], b[1]);
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, dpp_u32<kDppXor1>(v));
+  v = max(v, dpp_u32<kDppXor2>(v));
+  v = max(v, dpp_u32<kDppHalfMirror>(v));
+  v = max(v, dpp_u32<kDppMirror>(v));
+  auto a = __builtin_amdgcn_permlane16_swap(v, v, false, false);
+  v = max(a[0], a[1]);
+  auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
+  return max(b[0], b[1]);
+}
 template <int MASK>
 __device__ __forceinline__ float xor_sum(float v) {
   return v + __shfl_xor(v, MASK, 64);
@@ -59,6 +123,20 @@ __device__ __forceinline__ float xor_sum(float v) {
 template <int MASK>
 __device__ __forceinline__ float xor_max(float v) {
   return fmaxf(v, __shfl_xor(v, MASK, 64));
+}
+// Inclusive prefix sum over the 64 lanes (row shifts, then row broadcasts).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ uint32_t dpp_shift_u32(uint32_t v) {  // invalid source lanes give 0
+  return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, CTRL, ROW_MASK, 0xF, false);
+}
+__device__ __forceinline__ uint32_t wave_incl_scan_u32(uint32_t v) {
+  v += dpp_shift_u32<0x111, 0xF>(v);  // row_shr:1
+  v += dpp_shift_u32<0x112, 0xF>(v);  // row_shr:2
+  v += dpp_shift_u32<0x114, 0xF>(v);  // row_shr:4
+  v += dpp_shift_u32<0x118, 0xF>(v);  // row_shr:8
+  v += dpp_shift_u32<0x142, 0xA>(v);  // row_bcast:15 into rows 1 and 3
+  v += dpp_shift_u32<0x143, 0xC>(v);  // row_bcast:31 into rows 2 and 3
+  return v;
 }
 
 // ------------------------------------------- cross-workgroup hand-off memory

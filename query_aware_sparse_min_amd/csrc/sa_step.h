@@ -8,6 +8,8 @@ namespace sa {
 // Query heads per kv-head the fused kernel is built for (larger groups run
 // the separate scorer / top-K / attention kernels).
 constexpr int kStepMaxGroup = 1;
+constexpr int kStepMaxPages = 4096;          // top-K keys of a list stay in registers
+constexpr int kStepMaxPhysPages = 1 << 27;   // resolved pages pack the page id in 27 bits
 
 // Control words at the head of the step workspace.
 struct StepCtl {
@@ -45,6 +47,7 @@ struct StepArgs {
   float* scores;    // [lists][max_pages]
   int32_t* sel;     // [lists][max_sel]
   int32_t* num_sel; // [lists]
+  int32_t* rsel;    // [lists][max_sel] kept pages resolved to (physical << 4) | (valid - 1)
   int max_sel;
   float* partials;  // [lists][ns][G][kHeadDim + 2]
   float* out;       // [B][hq][kHeadDim]
@@ -54,7 +57,9 @@ struct StepArgs {
 
 StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_cus);
 // Workgroups of the fused kernel that fit on the device at once (0 on error).
-int step_resident_wgs(int kv_dtype, int q_dtype, int num_cus);
+int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus);
+// Top-K keys per thread of the fused kernel for lists of up to max_pages pages.
+int step_kpt(int max_pages);
 size_t step_ctl_bytes(int lists);
 hipError_t launch_quest_step(int kv_dtype, int q_dtype, const StepArgs& A, const StepPlan& P,
                              hipStream_t st);

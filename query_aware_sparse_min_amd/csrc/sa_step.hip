@@ -16,7 +16,8 @@
 // for their completion, then a relaxed counter:
 //   score chunk -> scores, then score_done[list] += 1; the chunk that brings
 //                  score_done to the chunk count runs the list's top-K at once
-//                  and publishes the page list with sel_ready = 1;
+//                  (also resolving the kept pages through the page table) and
+//                  publishes the page lists with sel_ready = 1;
 //   attention   -> waits sel_ready; partial record, then attn_done += 1; the
 //                  split that brings attn_done to the split count merges the
 //                  list's partials into out and clears the list's counters.
@@ -33,7 +34,6 @@ namespace {
 constexpr int kStepThreads = 256;
 constexpr int kScoreIT = 8;               // loads per lane per score pass
 constexpr int kScorePass = 8 * kScoreIT;  // pages per score pass (64)
-constexpr int kTopkCap = 4096;            // keys staged in LDS (longer lists re-read scores)
 constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling (each poll is a memory round trip)
 
 // Thread 0 waits until *p >= target; the workgroup then continues.
@@ -63,12 +63,12 @@ __device__ __forceinline__ uint32_t publish_add(uint32_t* ctr) {
 
 template <int KT, int QT, int G>
 union StepSmem {
-  TopkSmem<kStepThreads, kTopkCap> topk;
+  TopkSmem<kStepThreads> topk;
   AttnSmem<G> attn;
-  MergeSmem merge;
 };
 
-template <int KT, int QT, int G>
+// KPT: top-K keys per thread in registers (lists of up to 256 * KPT pages).
+template <int KT, int QT, int G, int KPT>
 __global__ __launch_bounds__(kStepThreads, 4) void quest_step_kernel(StepArgs A, StepPlan P) {
   __shared__ StepSmem<KT, QT, G> sm;
   __shared__ int s_flag;
@@ -97,9 +97,10 @@ __global__ __launch_bounds__(kStepThreads, 4) void quest_step_kernel(StepArgs A,
       if (tid == 0) s_flag = old == (uint32_t)(P.nc - 1);
       __syncthreads();
       if (s_flag) {  // the list's last chunk: every score is in, select now
-        topk_list<kStepThreads, kTopkCap, true>(sc_row, n, n, 1, A.k_compete, A.n_head, A.n_tail,
+        topk_list<kStepThreads, KPT, true>(sc_row, n, n, 1, A.k_compete, A.n_head, A.n_tail,
                                                 A.sel + (size_t)i * A.max_sel, A.num_sel + i,
-                                                A.max_sel, sm.topk);
+                                                A.max_sel, sm.topk, pt_row, L, A.num_pages,
+                                                A.rsel + (size_t)i * A.max_sel);
         publish_add(&lc->sel_ready);
       }
     } else {  // -------------------------------------------------------- attention split
@@ -110,13 +111,12 @@ __global__ __launch_bounds__(kStepThreads, 4) void quest_step_kernel(StepArgs A,
       attend_range<KT, QT, G, 1, true>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
                                        pt_row, L, A.sel + (size_t)i * A.max_sel, j0, j1,
                                        A.scale_log2, part_list + (size_t)idx * G * kPartStride,
-                                       sm.attn);
+                                       sm.attn, A.rsel + (size_t)i * A.max_sel);
       const uint32_t old = publish_add(&lc->attn_done);
       if (tid == 0) s_flag = old == (uint32_t)(P.ns - 1);
       __syncthreads();
       if (s_flag) {
-        merge_list<true>(part_list, P.ns, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim,
-                         sm.merge);
+        merge_list<true>(part_list, P.ns, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim);
         if (tid == 0) {  // every task of this list has finished: clear its counters
           st_x<true>(&lc->score_done, 0u);
           st_x<true>(&lc->sel_ready, 0u);
@@ -129,14 +129,21 @@ __global__ __launch_bounds__(kStepThreads, 4) void quest_step_kernel(StepArgs A,
 }
 
 template <int KT, int QT>
-hipError_t step_dispatch_g(int G, const StepArgs& A, const StepPlan& P, hipStream_t st) {
-#define SA_ST(GG)                                                                        \
-  hipLaunchKernelGGL((quest_step_kernel<KT, QT, GG>), dim3(P.grid), dim3(kStepThreads), 0, st, \
-                     A, P)
-  (void)G;  // the fused kernel is built for G == 1 (kStepMaxGroup)
-  SA_ST(1);
-#undef SA_ST
+hipError_t step_dispatch(int kpt, const StepArgs& A, const StepPlan& P, hipStream_t st) {
+  if (kpt <= 8)
+    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 8>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
+  else
+    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 16>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
   return hipGetLastError();
+}
+
+template <int KT, int QT>
+int resident_of(int kpt) {
+  int per_cu = 0;
+  const hipError_t e = kpt <= 8
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 8>, kStepThreads, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 16>, kStepThreads, 0);
+  return e == hipSuccess ? per_cu : 0;
 }
 
 }  // namespace
@@ -145,7 +152,7 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
   StepPlan P{};
   P.lists = B * Hkv;
   const long lists = P.lists;
-  const int G = Hq / Hkv;
+  (void)Hq;
   const long wgs = (long)num_cus * 4;  // resident workgroups aimed for
   // score chunks: about one per resident workgroup overall, whole passes of 64 pages
   long chunk = (lists * max_pages + wgs - 1) / wgs;
@@ -156,8 +163,6 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
   // attention splits: about one per resident workgroup, >= 4 pages (one per wave)
   long pps = (lists * max_sel + wgs - 1) / wgs;
   if (pps < 4) pps = 4;
-  const long min_pps = (max_sel * (long)G + 2047) / 2048;  // merge keeps ns * G weights in LDS
-  if (pps < min_pps) pps = min_pps;
   P.pps = (int)pps;
   P.ns = (int)((max_sel + pps - 1) / pps);
   P.n_tasks = (int)(lists * (P.nc + P.ns));
@@ -167,29 +172,25 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
 
 size_t step_ctl_bytes(int lists) { return sizeof(StepCtl) + (size_t)lists * sizeof(ListCtl); }
 
-int step_resident_wgs(int kv_dtype, int q_dtype, int num_cus) {
-  int per_cu = 0;
-  hipError_t e;
+int step_kpt(int max_pages) { return max_pages <= kStepThreads * 8 ? 8 : 16; }
+
+int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus) {
+  int per_cu;
   if (kv_dtype == SA_F32)
-    e = q_dtype == SA_F32
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<SA_F32, SA_F32, 1>, kStepThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<SA_F32, SA_BF16, 1>, kStepThreads, 0);
+    per_cu = q_dtype == SA_F32 ? resident_of<SA_F32, SA_F32>(kpt) : resident_of<SA_F32, SA_BF16>(kpt);
   else
-    e = q_dtype == SA_F32
-            ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<SA_BF16, SA_F32, 1>, kStepThreads, 0)
-            : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<SA_BF16, SA_BF16, 1>, kStepThreads, 0);
-  if (e != hipSuccess || per_cu < 1) return 0;
-  return per_cu * num_cus;
+    per_cu = q_dtype == SA_F32 ? resident_of<SA_BF16, SA_F32>(kpt) : resident_of<SA_BF16, SA_BF16>(kpt);
+  return per_cu < 1 ? 0 : per_cu * num_cus;
 }
 
 hipError_t launch_quest_step(int kv_dtype, int q_dtype, const StepArgs& A, const StepPlan& P,
                              hipStream_t st) {
-  const int G = A.hq / A.hkv;
+  const int kpt = step_kpt(A.max_pages);
   if (kv_dtype == SA_F32)
-    return q_dtype == SA_F32 ? step_dispatch_g<SA_F32, SA_F32>(G, A, P, st)
-                             : step_dispatch_g<SA_F32, SA_BF16>(G, A, P, st);
-  return q_dtype == SA_F32 ? step_dispatch_g<SA_BF16, SA_F32>(G, A, P, st)
-                           : step_dispatch_g<SA_BF16, SA_BF16>(G, A, P, st);
+    return q_dtype == SA_F32 ? step_dispatch<SA_F32, SA_F32>(kpt, A, P, st)
+                             : step_dispatch<SA_F32, SA_BF16>(kpt, A, P, st);
+  return q_dtype == SA_F32 ? step_dispatch<SA_BF16, SA_F32>(kpt, A, P, st)
+                           : step_dispatch<SA_BF16, SA_BF16>(kpt, A, P, st);
 }
 
 }  // namespace sa
