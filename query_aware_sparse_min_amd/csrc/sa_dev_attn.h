@@ -134,8 +134,8 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     if (j >= j1) return pr;
     const int x = (j - j0 - wave) >> 2;  // wave-uniform
     if (x < 64) {
-      pr.pp = __shfl(my_pp, x, 64);
-      pr.nv = __shfl(my_nv, x, 64);
+      pr.pp = __builtin_amdgcn_readlane(my_pp, x);
+      pr.nv = __builtin_amdgcn_readlane(my_nv, x);
       return pr;
     }
     if (rlst) {  // wave with more than 64 pages
@@ -189,15 +189,11 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
           float s = 0.0f;
 #pragma unroll
           for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[e], s);
-          s = xor_sum<1>(s);
-          s = xor_sum<2>(s);
-          s = xor_sum<4>(s);
-          s = xor_sum<8>(s);
+          s = sum16(s);
           z[it] = (4 * it + r < pg[u].nv) ? s * (scale_log2 * ksc[u][it]) : -INFINITY;
         }
         float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
-        pm = xor_max<16>(pm);
-        pm = xor_max<32>(pm);
+        pm = pair32_max(pair16_max(pm));
         const float mn = fmaxf(m[g], pm);  // finite: slot 0 of a kept page is valid
         const float alpha = exp2f(m[g] - mn);
         float pr[4], psum = 0.0f;
@@ -225,9 +221,9 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
   // fold the four token rows of each wave, then the four waves
 #pragma unroll
   for (int g = 0; g < G; ++g) {
-    l[g] = xor_sum<32>(xor_sum<16>(l[g]));
+    l[g] = pair32_sum(pair16_sum(l[g]));
 #pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = xor_sum<32>(xor_sum<16>(acc[g][e]));
+    for (int e = 0; e < 8; ++e) acc[g][e] = pair32_sum(pair16_sum(acc[g][e]));
   }
   if (r == 0) {
 #pragma unroll

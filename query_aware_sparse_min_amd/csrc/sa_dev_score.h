@@ -7,7 +7,7 @@
 // sum_i max(q_gi m_i, q_gi M_i), evaluated as q+ . M + q- . m with
 // q+ = max(q, 0), q- = min(q, 0).  A lane owns 8 dimensions of either the M
 // row or the m row of a (page, kv-head) record, so one 64-lane load covers two
-// pages in coalesced 256-byte rows; a 32-lane tree finishes each sum.  The
+// pages in coalesced 256-byte rows; a 32-lane all-reduce finishes each sum.  The
 // metadata is head-major, [Hkv][num_pages][2][d], so the records of one list's
 // pages lie next to each other when its pages do.
 #pragma once
@@ -68,11 +68,7 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
       float s = 0.0f;
 #pragma unroll
       for (int e = 0; e < 8; ++e) s = fmaf(qs[g][e], xv[e], s);
-      s = xor_sum<1>(s);
-      s = xor_sum<2>(s);
-      s = xor_sum<4>(s);
-      s = xor_sum<8>(s);
-      s = xor_sum<16>(s);
+      s = pair16_sum(sum16(s));
       best = fmaxf(best, s);
     }
     if ((lane & 31) == 0 && pg[it] < p1) st_x<COH>(sc_row + pg[it], ok ? best : -INFINITY);

@@ -11,15 +11,17 @@
 //
 // Method (no sort): every thread owns a contiguous run of middle units and
 // keeps their order-preserving uint32 keys in registers (scores -> keys with
-// -0.0 folded into +0.0).  The block min/max of the keys gives their common
-// high-bit prefix, which is skipped; radix-select passes over 12-bit digits
-// (LDS histograms used alternately, 16 bins per thread scanned from the
-// largest digit) find the exact k-th largest key T and how many T-valued keys
-// r are kept -- two passes for score sets that share sign and exponent.  One
-// block scan of (#keys > T, #keys == T) then ranks every kept unit in index
-// order: a unit equal to T is kept iff fewer than r equal units precede it
-// (the lower-index tie rule), and its rank is its output slot, so the list
-// comes out ascending without sorting.
+// -0.0 folded into +0.0).  The block min/max of the keys fixes their common
+// high bits.  Radix-select passes over 8-bit digits of the undetermined bits
+// then narrow a threshold prefix: LDS histogram by atomics, one barrier, and
+// every wave scans all 256 bins itself (4 per lane, DPP prefix sum, ballot)
+// so that all waves agree on the digit without a second barrier.  Three
+// histograms rotate, each cleared two passes before its next use.  The passes
+// stop once the threshold prefix is fully determined or once every key that
+// carries it is kept.  One block scan of (#keys above, #keys at the threshold)
+// then ranks every kept unit in index order: a unit at the threshold is kept
+// iff fewer than r such units precede it (the lower-index tie rule), and its
+// rank is its output slot, so the list comes out ascending without sorting.
 //
 // Lists longer than NT * KPT units use the same passes with the keys re-read
 // from the scores (KPT = 0).
@@ -29,15 +31,13 @@
 
 namespace sa {
 
-constexpr int kTopkDigit = 12;
+constexpr int kTopkDigit = 8;
 constexpr int kTopkBins = 1 << kTopkDigit;
 
 template <int NT>
 struct TopkSmem {
-  uint32_t hist[2][kTopkBins];
+  alignas(16) uint32_t hist[3][kTopkBins];
   uint32_t wmin[NT / 64], wmax[NT / 64];
-  uint32_t wsum[2][NT / 64];
-  uint32_t bc[2][2];
   uint32_t wa[NT / 64], wb[NT / 64];
   int last_kept;
 };
@@ -85,35 +85,31 @@ __device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, i
   const int r0 = min(tid * run, m);
   const int cnt_t = min(run, m - r0);
 
-  // keys (and, when resolving, page-table entries) of the run: one round trip.
-  // Loads are unconditional from clamped in-range indices so that they are all
-  // in flight together; out-of-run values are discarded afterwards.
+  // keys (and, when resolving, page-table entries) of the run and of the
+  // forced units: one round trip.  Loads are unconditional from clamped
+  // in-range indices so that they are all in flight together; out-of-run
+  // values are discarded afterwards.  Page-table entries stay raw until the
+  // emission so that nothing waits for them before then.
   uint32_t key[KPT > 0 ? KPT : 1];
-  int32_t rp[KPT > 0 ? KPT : 1];
+  int32_t pv[KPT > 0 ? KPT : 1];
   if constexpr (KPT > 0) {
     float v[KPT];
-    int32_t pv[KPT];
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int u = min(r0 + j, m - 1);
-      v[j] = ld_x<COH>(msc + u);
-      if (rout) pv[j] = pt_row[n_head + u];
+    for (int j = 0; j < KPT; ++j) v[j] = ld_x<COH>(msc + min(r0 + j, m - 1));
+    if (rout) {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) pv[j] = pt_row[n_head + min(r0 + j, m - 1)];
     }
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) {
-      const int u = min(r0 + j, m - 1);
-      key[j] = j < cnt_t ? order_key(v[j]) : 0u;
-      rp[j] = (rout && j < cnt_t) ? resolved_page(pv[j], min(kPage, L - (n_head + u) * kPage), num_pages) : -1;
-    }
+    for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? order_key(v[j]) : 0u;
   }
-  // forced units' resolved pages, fetched now as well
-  int32_t forced_rp = -1;
-  if (rout) {
-    const int c = min(tid, n_head + n_tail - 1);
-    const int u = c < 0 ? 0 : (c < n_head ? c : n - n_tail + (c - n_head));
-    const int32_t pv = pt_row[u];
-    if (tid < n_head + n_tail) forced_rp = resolved_page(pv, min(kPage, L - u * kPage), num_pages);
-  }
+  const int nf = n_head + n_tail;
+  const int fc = min(tid, nf > 0 ? nf - 1 : 0);
+  const int fu = nf == 0 ? 0 : (fc < n_head ? fc : n - n_tail + (fc - n_head));  // this thread's forced unit
+  const int32_t fpv = rout ? pt_row[fu] : -1;
+  auto resolve_raw = [&](int32_t pp, int u) -> int32_t {
+    return resolved_page(pp, min(kPage, L - u * kPage), num_pages);
+  };
   auto key_at = [&](int j) -> uint32_t {
     if constexpr (KPT > 0) return key[j];
     else return order_key(ld_x<COH>(msc + r0 + j));
@@ -128,94 +124,75 @@ __device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, i
     }
   };
 
-  {
-    uint4* h4 = reinterpret_cast<uint4*>(&sm.hist[0][0]);
-    for (int i = tid; i < 2 * kTopkBins / 4; i += NT) h4[i] = make_uint4(0u, 0u, 0u, 0u);
-  }
+  for (int i = tid; i < 3 * kTopkBins; i += NT) (&sm.hist[0][0])[i] = 0u;
   if (tid == 0) sm.last_kept = n_tail > 0 ? 1 : 0;
 
-  uint32_t T = 0xFFFFFFFFu, rem = 0;
+  // threshold: keys whose bits under mask dm equal tval; rem of them are kept
+  uint32_t dm = 0xFFFFFFFFu, tval = 0xFFFFFFFFu, rem = 0;
   if (k > 0) {
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for_keys([&](int, uint32_t x) { kmin = min(kmin, x); kmax = max(kmax, x); });
-#pragma unroll
-    for (int d = 1; d < 64; d <<= 1) {
-      kmin = min(kmin, (uint32_t)__shfl_xor((int)kmin, d, 64));
-      kmax = max(kmax, (uint32_t)__shfl_xor((int)kmax, d, 64));
-    }
+    kmin = wave_min_u32(kmin);
+    kmax = wave_max_u32(kmax);
     if (lane == 0) { sm.wmin[wave] = kmin; sm.wmax[wave] = kmax; }
     __syncthreads();  // also orders the histogram clears before the first pass
 #pragma unroll
     for (int w = 0; w < NW; ++w) { kmin = min(kmin, sm.wmin[w]); kmax = max(kmax, sm.wmax[w]); }
     rem = (uint32_t)k;
     const uint32_t diff = kmin ^ kmax;
-    if (diff == 0u) {
-      T = kmax;  // all keys equal: the k lowest indices are kept
-    } else {
-      int nb = 32 - __clz(diff);               // bits still undetermined
-      uint64_t prefix = (uint64_t)kmax >> nb;  // the determined high bits
-      for (int pass = 0; nb > 0; ++pass) {
+    tval = kmax;
+    if (diff != 0u) {
+      int nb = 32 - __clz(diff);  // low bits still undetermined
+      dm = nb >= 32 ? 0u : 0xFFFFFFFFu << nb;
+      tval = kmax & dm;
+      for (int pass = 0;; ++pass) {
         const int w = nb < kTopkDigit ? nb : kTopkDigit;
         const int shift = nb - w;
-        const int nbins = 1 << w;
-        uint32_t* H = sm.hist[pass & 1];
+        const int off = kTopkBins - (1 << w);  // bin of digit 0: the largest digit is bin 255
+        const uint32_t dmask = (1u << w) - 1u;
+        uint32_t* H = sm.hist[pass % 3];
         for_keys([&](int, uint32_t x) {
-          if (((uint64_t)x >> nb) == prefix) atomicAdd(&H[(x >> shift) & (uint32_t)(nbins - 1)], 1u);
+          if ((x & dm) == tval) atomicAdd(&H[off + (int)((x >> shift) & dmask)], 1u);
         });
         __syncthreads();
-        {  // clear the other histogram for the next pass (its last reads preceded this pass)
-          uint4* o4 = reinterpret_cast<uint4*>(&sm.hist[(pass + 1) & 1][0]);
-          for (int i = tid; i < kTopkBins / 4; i += NT) o4[i] = make_uint4(0u, 0u, 0u, 0u);
+        {  // last read one pass ago, next counted into two passes ahead
+          uint32_t* C = sm.hist[(pass + 2) % 3];
+          for (int i = tid; i < kTopkBins; i += NT) C[i] = 0u;
         }
-        // thread t scans bins nbins-1-16t down to nbins-16-16t (largest digits first)
-        constexpr int BPT = kTopkBins / NT;
-        uint32_t tot = 0;
-#pragma unroll
-        for (int jj = 0; jj < BPT; ++jj) {
-          const int bin = nbins - 1 - (BPT * tid + jj);
-          tot += bin >= 0 ? H[bin] : 0u;
-        }
-        uint32_t incl = tot;
-#pragma unroll
-        for (int d = 1; d < 64; d <<= 1) {
-          const uint32_t u = __shfl_up(incl, d, 64);
-          if (lane >= d) incl += u;
-        }
-        if (lane == 63) sm.wsum[pass & 1][wave] = incl;
-        __syncthreads();
+        // every wave: lane l holds bins 255-4l .. 252-4l, largest first
+        const uint4 hv = *reinterpret_cast<const uint4*>(&H[kTopkBins - 4 - 4 * lane]);
+        const uint32_t tot = hv.x + hv.y + hv.z + hv.w;
+        const uint32_t incl = wave_incl_scan_u32(tot);
         uint32_t before = incl - tot;
+        const uint64_t hit = __ballot(before < rem && rem <= incl);  // exactly one lane
+        const int src = __ffsll((unsigned long long)hit) - 1;
+        int bin = 0;
+        uint32_t cbin = 0, nrem = 0;
+        const uint32_t c4[4] = {hv.w, hv.z, hv.y, hv.x};
 #pragma unroll
-        for (int w2 = 0; w2 < NW; ++w2)
-          if (w2 < wave) before += sm.wsum[pass & 1][w2];
-        if (before < rem && rem <= before + tot) {  // the k-th key's digit is in this thread's bins
-          for (int jj = 0; jj < BPT; ++jj) {
-            const int bin = nbins - 1 - (BPT * tid + jj);
-            const uint32_t cj = bin >= 0 ? H[bin] : 0u;
-            if (before < rem && rem <= before + cj) {
-              sm.bc[pass & 1][0] = (uint32_t)bin;
-              sm.bc[pass & 1][1] = rem - before;
-            }
-            before += cj;
+        for (int jj = 0; jj < 4; ++jj) {
+          if (before < rem && rem <= before + c4[jj]) {
+            bin = kTopkBins - 1 - 4 * lane - jj;
+            cbin = c4[jj];
+            nrem = rem - before;
           }
+          before += c4[jj];
         }
-        __syncthreads();
-        prefix = (prefix << w) | sm.bc[pass & 1][0];
-        rem = sm.bc[pass & 1][1];
+        bin = __builtin_amdgcn_readlane(bin, src);
+        cbin = (uint32_t)__builtin_amdgcn_readlane((int)cbin, src);
+        rem = (uint32_t)__builtin_amdgcn_readlane((int)nrem, src);
+        tval |= (uint32_t)(bin - off) << shift;
+        dm |= dmask << shift;
         nb = shift;
+        if (nb == 0 || cbin == rem) break;  // fully determined, or the whole bin is kept
       }
-      T = (uint32_t)prefix;
     }
   }
 
-  // rank the kept middle units in index order: one block scan of (#> T, #== T)
+  // rank the kept middle units in index order: one block scan of (#above, #at) the threshold
   uint32_t gt = 0, eq = 0;
-  if (k > 0) for_keys([&](int, uint32_t x) { gt += x > T; eq += x == T; });
-  uint32_t ga = gt, ea = eq;
-#pragma unroll
-  for (int d = 1; d < 64; d <<= 1) {
-    const uint32_t ug = __shfl_up(ga, d, 64), ue = __shfl_up(ea, d, 64);
-    if (lane >= d) { ga += ug; ea += ue; }
-  }
+  if (k > 0) for_keys([&](int, uint32_t x) { gt += (x & dm) > tval; eq += (x & dm) == tval; });
+  const uint32_t ga = wave_incl_scan_u32(gt), ea = wave_incl_scan_u32(eq);
   if (lane == 63) { sm.wa[wave] = ga; sm.wb[wave] = ea; }
   __syncthreads();
   uint32_t gt_before = ga - gt, eq_before = ea - eq;
@@ -237,46 +214,34 @@ __device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, i
   if (k > 0) {
     uint32_t kept_before = gt_before + min(eq_before, rem);
     uint32_t eq_seen = eq_before;
+    auto visit = [&](int j, uint32_t x, int32_t praw) {
+      const uint32_t xm = x & dm;
+      bool keep = xm > tval;
+      if (xm == tval) {
+        keep = eq_seen < rem;
+        ++eq_seen;
+      }
+      if (keep) {
+        const int u = n_head + r0 + j;
+        emit(n_head + (int)kept_before, u, rout ? resolve_raw(praw, u) : -1);
+        ++kept_before;
+        if (u == n - 1) sm.last_kept = 1;
+      }
+    };
     if constexpr (KPT > 0) {
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        if (j < cnt_t) {
-          const uint32_t x = key[j];
-          bool keep = x > T;
-          if (x == T) {
-            keep = eq_seen < rem;
-            ++eq_seen;
-          }
-          if (keep) {
-            emit(n_head + (int)kept_before, n_head + r0 + j, rp[j]);
-            ++kept_before;
-            if (n_head + r0 + j == n - 1) sm.last_kept = 1;
-          }
-        }
-      }
+      for (int j = 0; j < KPT; ++j)
+        if (j < cnt_t) visit(j, key[j], rout ? pv[j] : -1);
     } else {
-      for (int j = 0; j < cnt_t; ++j) {
-        const uint32_t x = key_at(j);
-        bool keep = x > T;
-        if (x == T) {
-          keep = eq_seen < rem;
-          ++eq_seen;
-        }
-        if (keep) {
-          const int u = n_head + r0 + j;
-          emit(n_head + (int)kept_before, u, rout ? resolve(u) : -1);
-          ++kept_before;
-          if (u == n - 1) sm.last_kept = 1;
-        }
-      }
+      for (int j = 0; j < cnt_t; ++j) visit(j, key_at(j), rout ? pt_row[n_head + r0 + j] : -1);
     }
   }
   // forced units: c < n_head is head unit c (rank c); else tail unit n - n_tail + j (rank n_head + k + j)
-  for (int c = tid; c < n_head + n_tail; c += NT) {
+  for (int c = tid; c < nf; c += NT) {
     const bool head = c < n_head;
     const int u = head ? c : n - n_tail + (c - n_head);
     const int rank = head ? c : n_head + k + (c - n_head);
-    emit(rank, u, c == tid ? forced_rp : (rout ? resolve(u) : -1));
+    emit(rank, u, rout ? resolve_raw(c == tid ? fpv : pt_row[u], u) : -1);
   }
   if (upu > 1 && n_tail == 0) __syncthreads();  // only then can the final unit be dropped
   const int kept_units = n_head + k + n_tail;

@@ -68,11 +68,9 @@ constexpr int kDppXor2 = 0x4E;        // quad_perm [2,3,0,1]
 constexpr int kDppHalfMirror = 0x141; // lane i <-> 7 - i within each 8 lanes
 constexpr int kDppMirror = 0x140;     // lane i <-> 15 - i within each 16 lanes
 
-// partner lane (l ^ 16) / (l ^ 32) values, exchanged in one VALU op
-__device__ __forceinline__ uint32_t swap16_u32(uint32_t v) {
-  const auto r = __builtin_amdgcn_permlane16_swap(v, v, false, false);
-  return r[0] == v ? r[1] : r[0];
-}
+// permlane16/32_swap exchange lane l's value with lane l ^ 16 / l ^ 32; of the
+// two results one is the lane's own value and the other the partner's, so a
+// commutative combine of both gives the pair result.
 __device__ __forceinline__ float sum16(float v) {  // all-reduce over each 16-lane row
   v += dpp_f32<kDppXor1>(v);
   v += dpp_f32<kDppXor2>(v);
@@ -115,14 +113,6 @@ __device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
   v = max(a[0], a[1]);
   auto b = __builtin_amdgcn_permlane32_swap(v, v, false, false);
   return max(b[0], b[1]);
-}
-template <int MASK>
-__device__ __forceinline__ float xor_sum(float v) {
-  return v + __shfl_xor(v, MASK, 64);
-}
-template <int MASK>
-__device__ __forceinline__ float xor_max(float v) {
-  return fmaxf(v, __shfl_xor(v, MASK, 64));
 }
 // Inclusive prefix sum over the 64 lanes (row shifts, then row broadcasts).
 template <int CTRL, int ROW_MASK>
