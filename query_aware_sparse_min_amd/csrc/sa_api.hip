@@ -118,7 +118,7 @@ int resident_step_wgs(int kv_dtype, int q_dtype, int max_pages) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   const int kpt = step_kpt(max_pages);
-  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1) + (kpt > 8 ? 4 : 0);
+  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1) + (kpt > 2 ? 4 : 0);
   if (dev < 64) {
     const int c = cache[dev][slot].load(std::memory_order_relaxed);
     if (c > 0) return c;
@@ -131,7 +131,7 @@ int resident_step_wgs(int kv_dtype, int q_dtype, int max_pages) {
 constexpr int kPlanCUs = 256;  // task decomposition is planned for a 256-CU MI355X
 
 struct StepLayout {
-  size_t ctl, scores, sel, num_sel, rsel, partials, total;
+  size_t ctl, scores, sel, num_sel, partials, total;
   int max_units, max_sel;
   bool dense;  // every list keeps all of its units: no scoring needed
   bool fused;  // Quest: one persistent kernel for the whole step
@@ -149,7 +149,7 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   const size_t lists = (size_t)s->batch * kv->num_kv_heads;
   L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel);
   L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
-  const size_t fused_part = (size_t)L.splan.lists * L.splan.ns * (hq / kv->num_kv_heads) * (kHeadDim + 2);
+  const size_t fused_part = (size_t)L.splan.lists * L.splan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2);
   size_t off = 0;
   L.ctl = off;
   off = align_up(off + step_ctl_bytes((int)lists));
@@ -159,8 +159,6 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   off = align_up(off + lists * L.max_sel * sizeof(int32_t));
   L.num_sel = off;
   off = align_up(off + lists * sizeof(int32_t));
-  L.rsel = off;
-  off = align_up(off + (L.fused ? lists * L.max_sel * sizeof(int32_t) : 0));
   L.partials = off;
   const size_t pf = L.plan.partial_floats > fused_part ? L.plan.partial_floats : fused_part;
   off = align_up(off + pf * sizeof(float));
@@ -332,7 +330,12 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
                                        nullptr, 0, lay.plan, softmax_scale, partials, out, st));
   }
   float* scores = reinterpret_cast<float*>(ws + lay.scores);
+  int wgs = 0;
   if (lay.fused) {
+    wgs = resident_step_wgs(kv->dtype, q_dtype, seqs->max_pages);
+    if (wgs < 1) wgs = device_cus();  // one workgroup per CU always fits
+  }
+  if (lay.fused && lay.splan.nc <= wgs) {
     StepArgs A{};
     A.q = q;
     A.k = kv->k;
@@ -350,17 +353,14 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
     A.n_tail = cfg->n_tail_forced;
     A.scale_log2 = softmax_scale * 1.4426950408889634f;
     A.scores = scores;
-    A.sel = sel_buf;
-    A.num_sel = num_buf;
-    A.rsel = reinterpret_cast<int32_t*>(ws + lay.rsel);
+    A.sel = sel;
+    A.num_sel = num_sel;
     A.max_sel = lay.max_sel;
     A.partials = partials;
     A.out = out;
     A.ctl = reinterpret_cast<StepCtl*>(ws + lay.ctl);
     A.lctl = reinterpret_cast<ListCtl*>(ws + lay.ctl + sizeof(StepCtl));
     StepPlan P = lay.splan;
-    int wgs = resident_step_wgs(kv->dtype, q_dtype, seqs->max_pages);
-    if (wgs < 1) wgs = device_cus();  // one workgroup per CU always fits
     P.grid = P.n_tasks < wgs ? P.n_tasks : wgs;
     return hip_status(launch_quest_step(kv->dtype, q_dtype, A, P, st));
   }

@@ -36,10 +36,11 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
 __global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __restrict__ partials,
                                                             int hkv, int G, int nsplit,
                                                             float* __restrict__ out) {
+  __shared__ float lds[3 * kAttnThreads];
   const int h = blockIdx.x, b = blockIdx.y;
   const size_t list = (size_t)b * hkv + h;
   merge_list(partials + list * nsplit * G * kPartStride, nsplit, G,
-             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim);
+             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, lds);
 }
 
 template <int KT, int QT>

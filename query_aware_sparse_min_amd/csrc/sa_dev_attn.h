@@ -1,5 +1,5 @@
 // sa_dev_attn.h - flash-decoding attention of one (batch, kv-head) list over
-// a range of its selected pages, inside one 256-thread workgroup, and the
+// a range of its selected pages, inside one workgroup of NW waves, and the
 // merge of the per-split partials (device code shared by the standalone
 // attention kernel and the fused decode-step kernel).
 //
@@ -8,7 +8,7 @@
 // int8 K/V gathered by the selection, rows split over cores then reduced.
 // "Day 10·2": the softmax is renormalised over the selected set only.
 //
-// Layout of the work: the four waves take the pages of the range in turn,
+// Layout of the work: the NW waves take the pages of the range in turn,
 // PW at a time so that 8 * PW row loads per lane are in flight.  Lane l owns token
 // row (l / 16) of a 4-row group and dimensions 8*(l % 16)..+7, so one 64-lane
 // load reads four whole rows of a page.  Scores are kept in base 2
@@ -23,10 +23,10 @@ namespace sa {
 
 constexpr int kPartStride = kHeadDim + 2;  // acc[d], max (base 2), sum
 
-template <int G>
+template <int G, int NW = 4>
 struct AttnSmem {
-  float acc[4][G][kHeadDim];
-  float m[4][G], l[4][G];
+  float acc[NW][G][kHeadDim];
+  float m[NW][G], l[NW][G];
 };
 
 // 8 elements of a K/V row as raw words (widened when used).
@@ -77,17 +77,18 @@ struct PageRef {
 
 // Attend to pages lst[j0 .. j1) (lst == nullptr: logical pages j0 .. j1) of
 // list (b, h) and write the workgroup's partial records to part[G][kPartStride].
-// rlst (optional) holds the same pages already resolved to
-// (physical page << 4) | (valid tokens - 1); the page table is then not read.
+// rlst (optional; LDS or memory written before the launch) holds the pages
+// already resolved to (physical page << 4) | (valid tokens - 1), read with
+// plain loads; the page table is then not read.
 // PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
-// COH: the page list is read and the partials are written device-coherently.
-template <int KT, int QT, int G, int PW = 2, bool COH = false>
+// COH: lst is read and the partials are written device-coherently.
+template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4>
 __device__ __forceinline__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
                              const void* __restrict__ v, const uint16_t* __restrict__ ks,
                              const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
                              const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
                              int j1, float scale_log2, float* __restrict__ part,
-                             AttnSmem<G>& sm, const int32_t* rlst = nullptr) {
+                             AttnSmem<G, NW>& sm, const int32_t* rlst = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int hq = hkv * G;
@@ -106,19 +107,19 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
   }
 
-  // Resolve this wave's pages j = j0 + wave + 4 * x (x < 64) up front: lane x
+  // Resolve this wave's pages j = j0 + wave + NW * x (x < 64) up front: lane x
   // loads list entry x, then its page-table entry, so the list and the page
   // table cost one memory round trip each instead of one per page.
   int my_pp = -1, my_nv = 0;
   if (rlst) {
-    const int j = j0 + wave + 4 * lane;
-    const int32_t r = j < j1 ? ld_x<COH>(rlst + j) : -1;
+    const int j = j0 + wave + NW * lane;
+    const int32_t r = j < j1 ? rlst[j] : -1;
     if (r >= 0) {
       my_pp = r >> 4;
       my_nv = (r & 15) + 1;
     }
   } else {
-    const int j = j0 + wave + 4 * lane;
+    const int j = j0 + wave + NW * lane;
     int p = -1;
     if (j < j1) p = lst ? ld_x<COH>(lst + j) : j;
     if (p >= 0 && p < np) {
@@ -132,14 +133,14 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
   auto page_of = [&](int j) -> PageRef {
     PageRef pr{-1, 0};
     if (j >= j1) return pr;
-    const int x = (j - j0 - wave) >> 2;  // wave-uniform
+    const int x = (j - j0 - wave) / NW;  // wave-uniform
     if (x < 64) {
       pr.pp = __builtin_amdgcn_readlane(my_pp, x);
       pr.nv = __builtin_amdgcn_readlane(my_nv, x);
       return pr;
     }
     if (rlst) {  // wave with more than 64 pages
-      const int32_t r = ld_x<COH>(rlst + j);
+      const int32_t r = rlst[j];
       if (r >= 0) {
         pr.pp = r >> 4;
         pr.nv = (r & 15) + 1;
@@ -155,13 +156,13 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     return pr;
   };
 
-  for (int jb = j0 + wave; jb < j1; jb += 4 * PW) {
+  for (int jb = j0 + wave; jb < j1; jb += NW * PW) {
     PageRef pg[PW];
     Raw8<KT> kr[PW][4], vr[PW][4];
     float ksc[PW][4], vsc[PW][4];
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
-      pg[u] = page_of(jb + 4 * u);
+      pg[u] = page_of(jb + NW * u);
       const int ppl = pg[u].pp >= 0 ? pg[u].pp : 0;  // empty slot: load page 0, result unused
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
@@ -176,9 +177,13 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
         }
       }
     }
+    // every K/V load of the iteration is issued before any of them is used
+    __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
-      if (pg[u].pp < 0) continue;  // wave-uniform
+      // an empty slot is masked (selects, no branch, so the loads above stay
+      // where they are): all its scores are -inf and it changes nothing
+      const bool live = pg[u].pp >= 0;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
         float z[4];
@@ -190,16 +195,17 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
 #pragma unroll
           for (int e = 0; e < 8; ++e) s = fmaf(qv[g][e], kx[e], s);
           s = sum16(s);
-          z[it] = (4 * it + r < pg[u].nv) ? s * (scale_log2 * ksc[u][it]) : -INFINITY;
+          z[it] = (live && 4 * it + r < pg[u].nv) ? s * (scale_log2 * ksc[u][it]) : -INFINITY;
         }
         float pm = fmaxf(fmaxf(z[0], z[1]), fmaxf(z[2], z[3]));
         pm = pair32_max(pair16_max(pm));
-        const float mn = fmaxf(m[g], pm);  // finite: slot 0 of a kept page is valid
-        const float alpha = exp2f(m[g] - mn);
+        const float mn = fmaxf(m[g], pm);  // -inf only while nothing has been attended
+        const bool none = mn == -INFINITY;
+        const float alpha = none ? 1.0f : exp2f(m[g] - mn);
         float pr[4], psum = 0.0f;
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
-          pr[it] = exp2f(z[it] - mn);
+          pr[it] = none ? 0.0f : exp2f(z[it] - mn);
           psum += pr[it];
           pr[it] *= vsc[u][it];
         }
@@ -218,7 +224,7 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     }
   }
 
-  // fold the four token rows of each wave, then the four waves
+  // fold the four token rows of each wave, then the NW waves
 #pragma unroll
   for (int g = 0; g < G; ++g) {
     l[g] = pair32_sum(pair16_sum(l[g]));
@@ -241,11 +247,11 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     const int g = idx / kHeadDim, dim = idx % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
-    for (int w = 0; w < 4; ++w) M = fmaxf(M, sm.m[w][g]);
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
     float a = 0.0f, ls = 0.0f;
     if (M != -INFINITY) {
 #pragma unroll
-      for (int w = 0; w < 4; ++w) {
+      for (int w = 0; w < NW; ++w) {
         const float f = exp2f(sm.m[w][g] - M);
         a = fmaf(sm.acc[w][g][dim], f, a);
         ls = fmaf(sm.l[w][g], f, ls);
@@ -260,29 +266,34 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
 }
 
 // Merge ns partial records part[ns][G][kPartStride] of one list into
-// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  Each
-// output element fetches the (acc, max, sum) of 16 splits at a time and folds
-// them into a running (M, acc, sum), so 16 splits cost one memory round trip.
-// COH: partials are read device-coherently.  All threads of the workgroup call.
+// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  The
+// workgroup's threads form P = blockDim / (G * 128) groups (at least one);
+// group p folds splits p, p + P, p + 2P, ... into a running (M, acc, sum),
+// fetching 16 splits per memory round trip, and the groups are combined
+// through lds (3 * blockDim floats).  The order is fixed, so the result is
+// deterministic.  COH: partials are read device-coherently.  All threads call.
 template <bool COH = false>
 __device__ __forceinline__ void merge_list(const float* __restrict__ part, int ns, int G,
-                                           float* __restrict__ out) {
+                                           float* __restrict__ out, float* __restrict__ lds) {
   constexpr int C = 16;
-  for (int o = threadIdx.x; o < G * kHeadDim; o += blockDim.x) {
+  const int no = G * kHeadDim;
+  const int nt = blockDim.x;
+  const int P = nt / no > 1 ? nt / no : 1;
+  // folds splits first, first + step, ... (< ns) of output o into (M, a, lsum)
+  auto fold = [&](int o, int first, int step, float& M, float& a, float& lsum) {
     const int g = o / kHeadDim, dim = o % kHeadDim;
-    float M = -INFINITY, a = 0.0f, lsum = 0.0f;
-    for (int s0 = 0; s0 < ns; s0 += C) {
+    for (int s0 = first; s0 < ns; s0 += C * step) {
       float av[C], mv[C], lv[C];
 #pragma unroll
       for (int j = 0; j < C; ++j) {  // unconditional loads (clamped split) stay in flight together
-        const float* rec = part + ((size_t)min(s0 + j, ns - 1) * G + g) * kPartStride;
+        const float* rec = part + ((size_t)min(s0 + j * step, ns - 1) * G + g) * kPartStride;
         av[j] = ld_x<COH>(rec + dim);
         mv[j] = ld_x<COH>(rec + kHeadDim);
         lv[j] = ld_x<COH>(rec + kHeadDim + 1);
       }
 #pragma unroll
       for (int j = 0; j < C; ++j)
-        if (s0 + j >= ns) lv[j] = 0.0f;
+        if (s0 + j * step >= ns) lv[j] = 0.0f;
       float Mc = M;
 #pragma unroll
       for (int j = 0; j < C; ++j)
@@ -301,7 +312,38 @@ __device__ __forceinline__ void merge_list(const float* __restrict__ part, int n
       }
       M = Mc;
     }
-    out[o] = lsum > 0.0f ? a / lsum : 0.0f;
+  };
+  if (P == 1) {
+    for (int o = threadIdx.x; o < no; o += nt) {
+      float M = -INFINITY, a = 0.0f, lsum = 0.0f;
+      fold(o, 0, 1, M, a, lsum);
+      out[o] = lsum > 0.0f ? a / lsum : 0.0f;
+    }
+    return;
+  }
+  const int t = threadIdx.x;
+  float M = -INFINITY, a = 0.0f, lsum = 0.0f;
+  if (t < P * no) fold(t % no, t / no, P, M, a, lsum);
+  lds[t] = M;
+  lds[nt + t] = a;
+  lds[2 * nt + t] = lsum;
+  __syncthreads();
+  if (t < no) {
+    float Mx = -INFINITY;
+    for (int p = 0; p < P; ++p)
+      if (lds[2 * nt + p * no + t] > 0.0f) Mx = fmaxf(Mx, lds[p * no + t]);
+    float at = 0.0f, lt = 0.0f;
+    if (Mx != -INFINITY) {
+      for (int p = 0; p < P; ++p) {
+        const float lp = lds[2 * nt + p * no + t];
+        if (lp > 0.0f) {
+          const float w = exp2f(lds[p * no + t] - Mx);
+          at = fmaf(lds[nt + p * no + t], w, at);
+          lt = fmaf(lp, w, lt);
+        }
+      }
+    }
+    out[t] = lt > 0.0f ? at / lt : 0.0f;
   }
 }
 

@@ -1,5 +1,5 @@
 // sa_dev_score.h - Quest page scores of a range of pages of one list inside
-// one 256-thread workgroup (device code shared by the standalone scorer and
+// one workgroup of NW waves (device code shared by the standalone scorer and
 // the fused decode-step kernel).
 //
 // "Quest 完全拆解" explainer, upper bound from min/max metadata and the GQA
@@ -16,14 +16,22 @@
 
 namespace sa {
 
-// Pages [p0, p1) of list (b, h); at most 8 * IT pages.  sc_row: the list's
-// scores (device-coherent stores when COH).  All 256 threads call.
-template <int KT, int QT, int G, int IT, bool COH = false>
-__device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
+// Pages [p0, p1) of list (b, h), at most 2 * NW * IT pages, p1 <= the page-table
+// row length max_pages; pages at or beyond the list's page count n score -inf.
+// n is ceil(min(*len_b, 16 max_pages) / 16), read after the page-table and
+// metadata loads have been issued so that they need not wait for it; the
+// function returns n.  sc_row: the list's scores (device-coherent stores when
+// COH).  pp_out (optional, LDS): the physical page of page p0 + j at [j], -1
+// when the page is invalid or its page-table entry is out of range.  All
+// 64 * NW threads call.
+template <int KT, int QT, int G, int IT, bool COH = false, int NW = 4>
+__device__ __forceinline__ int quest_score_range(const void* __restrict__ q,
                                                   const void* __restrict__ meta, int num_pages,
                                                   int hkv, int b, int h,
                                                   const int32_t* __restrict__ pt_row, int p0,
-                                                  int p1, float* __restrict__ sc_row) {
+                                                  int p1, const int32_t* __restrict__ len_b,
+                                                  int max_pages, float* __restrict__ sc_row,
+                                                  int32_t* pp_out = nullptr) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int half = lane >> 5, row = (lane >> 4) & 1, c = lane & 15;
   const int hq = hkv * G;
@@ -34,7 +42,7 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
   int ppg[IT];
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const int p = p0 + 2 * (wave + 4 * it) + half;
+    const int p = p0 + 2 * (wave + NW * it) + half;
     pg[it] = p;
     ppg[it] = pt_row[min(p, p1 - 1)];
   }
@@ -44,6 +52,7 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
     const int pp = (ppg[it] >= 0 && ppg[it] < num_pages) ? ppg[it] : 0;
     x[it].load(meta, (((size_t)h * num_pages + pp) * 2 + row) * kHeadDim + 8 * c);
   }
+  const int n_valid = (clamp_len(*len_b, max_pages) + kPage - 1) / kPage;
   float qs[G][8];
 #pragma unroll
   for (int g = 0; g < G; ++g) {
@@ -54,14 +63,13 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
   }
 #pragma unroll
   for (int it = 0; it < IT; ++it) {
-    const bool ok = pg[it] < p1 && ppg[it] >= 0 && ppg[it] < num_pages;
+    const bool ok = pg[it] < p1 && pg[it] < n_valid && ppg[it] >= 0 && ppg[it] < num_pages;
+    // unconditional use of the loaded words (a select, not a branch), so the
+    // compiler cannot sink the load into a branch behind the others
     float xv[8];
-    if (ok) {
-      x[it].get(xv);
-    } else {
+    x[it].get(xv);
 #pragma unroll
-      for (int e = 0; e < 8; ++e) xv[e] = 0.0f;
-    }
+    for (int e = 0; e < 8; ++e) xv[e] = ok ? xv[e] : 0.0f;
     float best = -INFINITY;
 #pragma unroll
     for (int g = 0; g < G; ++g) {
@@ -71,8 +79,12 @@ __device__ __forceinline__ void quest_score_range(const void* __restrict__ q,
       s = pair16_sum(sum16(s));
       best = fmaxf(best, s);
     }
-    if ((lane & 31) == 0 && pg[it] < p1) st_x<COH>(sc_row + pg[it], ok ? best : -INFINITY);
+    if ((lane & 31) == 0 && pg[it] < p1) {
+      st_x<COH>(sc_row + pg[it], ok ? best : -INFINITY);
+      if (pp_out) pp_out[pg[it] - p0] = ok ? ppg[it] : -1;
+    }
   }
+  return n_valid;
 }
 
 }  // namespace sa

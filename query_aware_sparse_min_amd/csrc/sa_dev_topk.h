@@ -24,7 +24,9 @@
 // rank is its output slot, so the list comes out ascending without sorting.
 //
 // Lists longer than NT * KPT units use the same passes with the keys re-read
-// from the scores (KPT = 0).
+// from the scores (KPT = 0).  The core hands every kept unit with its output
+// rank to a caller-supplied function, so a caller can write the list, or keep
+// only the units of its own page range.
 #pragma once
 
 #include "sa_internal.h"
@@ -48,35 +50,20 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// A kept page as the attention tasks read it: (physical page << 4) | (valid tokens - 1),
-// or -1 when the page-table entry is out of range.
-__device__ __forceinline__ int32_t resolved_page(int pp, int nv, int num_pages) {
-  return (pp >= 0 && pp < num_pages) ? ((pp << 4) | (nv - 1)) : -1;
-}
-
-// Selection of one list.  sc: the list's scores (unit 0 first, n units, np
-// pages, upu pages per unit).  KPT > 0 requires n - n_head - n_tail <= NT * KPT.
-// COH: scores are read and outputs written device-coherently.  rout (optional,
-// upu == 1 only): the kept pages resolved through pt_row as resolved_page().
-// All NT threads call.
-template <int NT, int KPT, bool COH>
-__device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, int np, int upu, int k, int n_head,
-                          int n_tail, int32_t* __restrict__ out, int32_t* __restrict__ out_n,
-                          int max_sel, TopkSmem<NT>& sm, const int32_t* __restrict__ pt_row = nullptr,
-                          int L = 0, int num_pages = 0, int32_t* __restrict__ rout = nullptr) {
+// Selection core of one list.  sc: the list's n unit scores.  Calls
+// keep(rank, u) exactly once for every kept unit u, where rank is u's position
+// among the kept units in ascending unit order (any thread may make a call).
+// KPT > 0 requires n - n_head - n_tail <= NT * KPT.  COH: the scores are read
+// device-coherently.  All NT threads call; sm is free again on return once the
+// caller has synchronised.
+template <int NT, int KPT, bool COH, typename Keep>
+__device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, int k, int n_head,
+                                          int n_tail, TopkSmem<NT>& sm, Keep&& keep) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  auto resolve = [&](int p) -> int32_t {
-    return resolved_page(pt_row[p], min(kPage, L - p * kPage), num_pages);
-  };
 
   if (n <= n_head + n_tail + k) {  // every unit is kept; no padding
-    const int cnt = min(np, max_sel);
-    for (int i = tid; i < max_sel; i += NT) {
-      st_x<COH>(out + i, i < cnt ? i : -1);
-      if (rout) st_x<COH>(rout + i, i < cnt ? resolve(i) : -1);
-    }
-    if (tid == 0) st_x<COH>(out_n, cnt);
+    for (int u = tid; u < n; u += NT) keep(u, u);
     return;
   }
   const int m = n - n_head - n_tail;  // competing middle units; m > k >= 0
@@ -85,31 +72,17 @@ __device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, i
   const int r0 = min(tid * run, m);
   const int cnt_t = min(run, m - r0);
 
-  // keys (and, when resolving, page-table entries) of the run and of the
-  // forced units: one round trip.  Loads are unconditional from clamped
+  // keys of the run: one round trip.  Loads are unconditional from clamped
   // in-range indices so that they are all in flight together; out-of-run
-  // values are discarded afterwards.  Page-table entries stay raw until the
-  // emission so that nothing waits for them before then.
+  // values are discarded afterwards.
   uint32_t key[KPT > 0 ? KPT : 1];
-  int32_t pv[KPT > 0 ? KPT : 1];
   if constexpr (KPT > 0) {
     float v[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) v[j] = ld_x<COH>(msc + min(r0 + j, m - 1));
-    if (rout) {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) pv[j] = pt_row[n_head + min(r0 + j, m - 1)];
-    }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? order_key(v[j]) : 0u;
   }
-  const int nf = n_head + n_tail;
-  const int fc = min(tid, nf > 0 ? nf - 1 : 0);
-  const int fu = nf == 0 ? 0 : (fc < n_head ? fc : n - n_tail + (fc - n_head));  // this thread's forced unit
-  const int32_t fpv = rout ? pt_row[fu] : -1;
-  auto resolve_raw = [&](int32_t pp, int u) -> int32_t {
-    return resolved_page(pp, min(kPage, L - u * kPage), num_pages);
-  };
   auto key_at = [&](int j) -> uint32_t {
     if constexpr (KPT > 0) return key[j];
     else return order_key(ld_x<COH>(msc + r0 + j));
@@ -125,7 +98,6 @@ __device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, i
   };
 
   for (int i = tid; i < 3 * kTopkBins; i += NT) (&sm.hist[0][0])[i] = 0u;
-  if (tid == 0) sm.last_kept = n_tail > 0 ? 1 : 0;
 
   // threshold: keys whose bits under mask dm equal tval; rem of them are kept
   uint32_t dm = 0xFFFFFFFFu, tval = 0xFFFFFFFFu, rem = 0;
@@ -200,56 +172,54 @@ __device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, i
   for (int w2 = 0; w2 < NW; ++w2)
     if (w2 < wave) { gt_before += sm.wa[w2]; eq_before += sm.wb[w2]; }
 
-  const int last_pages = np - (n - 1) * upu;  // pages of the final (possibly partial) unit
-  auto emit = [&](int rank, int u, int32_t r) {
-    const int cntp = (u == n - 1) ? last_pages : upu;
-    for (int i = 0; i < cntp; ++i) {
-      const int pos = rank * upu + i;
-      if (pos < max_sel) {
-        st_x<COH>(out + pos, u * upu + i);
-        if (rout) st_x<COH>(rout + pos, r);
-      }
-    }
-  };
   if (k > 0) {
     uint32_t kept_before = gt_before + min(eq_before, rem);
     uint32_t eq_seen = eq_before;
-    auto visit = [&](int j, uint32_t x, int32_t praw) {
+    for_keys([&](int j, uint32_t x) {
       const uint32_t xm = x & dm;
-      bool keep = xm > tval;
+      bool kp = xm > tval;
       if (xm == tval) {
-        keep = eq_seen < rem;
+        kp = eq_seen < rem;
         ++eq_seen;
       }
-      if (keep) {
-        const int u = n_head + r0 + j;
-        emit(n_head + (int)kept_before, u, rout ? resolve_raw(praw, u) : -1);
+      if (kp) {
+        keep(n_head + (int)kept_before, n_head + r0 + j);
         ++kept_before;
-        if (u == n - 1) sm.last_kept = 1;
       }
-    };
-    if constexpr (KPT > 0) {
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (j < cnt_t) visit(j, key[j], rout ? pv[j] : -1);
-    } else {
-      for (int j = 0; j < cnt_t; ++j) visit(j, key_at(j), rout ? pt_row[n_head + r0 + j] : -1);
-    }
+    });
   }
   // forced units: c < n_head is head unit c (rank c); else tail unit n - n_tail + j (rank n_head + k + j)
-  for (int c = tid; c < nf; c += NT) {
+  for (int c = tid; c < n_head + n_tail; c += NT) {
     const bool head = c < n_head;
-    const int u = head ? c : n - n_tail + (c - n_head);
-    const int rank = head ? c : n_head + k + (c - n_head);
-    emit(rank, u, rout ? resolve_raw(c == tid ? fpv : pt_row[u], u) : -1);
+    keep(head ? c : n_head + k + (c - n_head), head ? c : n - n_tail + (c - n_head));
   }
-  if (upu > 1 && n_tail == 0) __syncthreads();  // only then can the final unit be dropped
-  const int kept_units = n_head + k + n_tail;
-  const int cnt = min(kept_units * upu - (sm.last_kept ? upu - last_pages : 0), max_sel);
-  for (int i = cnt + tid; i < max_sel; i += NT) {
-    st_x<COH>(out + i, -1);
-    if (rout) st_x<COH>(rout + i, -1);
-  }
+}
+
+// Selection of one list written as a page list.  sc: the list's scores (unit 0
+// first, n units, np pages, upu pages per unit).  out: the kept units' pages
+// in ascending order, then -1 up to max_sel; out_n: their count.
+template <int NT, int KPT, bool COH>
+__device__ __forceinline__ void topk_list(const float* __restrict__ sc, int n, int np, int upu, int k,
+                                          int n_head, int n_tail, int32_t* __restrict__ out,
+                                          int32_t* __restrict__ out_n, int max_sel,
+                                          TopkSmem<NT>& sm) {
+  const int tid = threadIdx.x;
+  const bool all = n <= n_head + n_tail + k;
+  // written before any barrier of the core, which orders it before the kept units' writes
+  if (tid == 0) sm.last_kept = (all || n_tail > 0) ? 1 : 0;
+  const int last_pages = np - (n - 1) * upu;  // pages of the final (possibly partial) unit
+  topk_core<NT, KPT, COH>(sc, n, k, n_head, n_tail, sm, [&](int rank, int u) {
+    const int cntp = (u == n - 1) ? last_pages : upu;
+    for (int i = 0; i < cntp; ++i) {
+      const int pos = rank * upu + i;
+      if (pos < max_sel) st_x<COH>(out + pos, u * upu + i);
+    }
+    if (u == n - 1 && !all) sm.last_kept = 1;
+  });
+  if (!all && upu > 1 && n_tail == 0) __syncthreads();  // only then can the final unit be dropped
+  const int kept_units = all ? n : n_head + k + n_tail;
+  const int cnt = n <= 0 ? 0 : min(kept_units * upu - (sm.last_kept ? upu - last_pages : 0), max_sel);
+  for (int i = cnt + tid; i < max_sel; i += NT) st_x<COH>(out + i, -1);
   if (tid == 0) st_x<COH>(out_n, cnt);
 }
 

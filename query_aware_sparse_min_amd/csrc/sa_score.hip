@@ -31,7 +31,7 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   const int p0 = blockIdx.x * kScorePagesPerWG;
   if (p0 >= n) return;
   quest_score_range<KT, QT, G, kScoreIT>(q, meta, num_pages, hkv, b, h, pt + (size_t)b * max_pages,
-                                         p0, min(p0 + kScorePagesPerWG, n),
+                                         p0, min(p0 + kScorePagesPerWG, n), lens + b, max_pages,
                                          scores + ((size_t)b * hkv + h) * max_pages);
 }
 

@@ -10,6 +10,7 @@ namespace sa {
 constexpr int kStepMaxGroup = 1;
 constexpr int kStepMaxPages = 4096;          // top-K keys of a list stay in registers
 constexpr int kStepMaxPhysPages = 1 << 27;   // resolved pages pack the page id in 27 bits
+constexpr int kStepMaxChunk = 1024;          // pages per chunk task (kept in LDS)
 
 // Control words at the head of the step workspace.
 struct StepCtl {
@@ -18,20 +19,17 @@ struct StepCtl {
   uint32_t pad[13];
 };
 struct ListCtl {  // one 64-byte record per (batch, kv-head) list
-  uint32_t score_done;
-  uint32_t sel_ready;
-  uint32_t attn_done;
-  uint32_t pad[13];
+  uint32_t score_done;  // chunks whose scores are stored
+  uint32_t attn_done;   // chunks whose partial record is stored
+  uint32_t pad[14];
 };
 
 struct StepPlan {
   int lists;        // B * Hkv
-  int chunk_pages;  // pages per score task
-  int nc;           // score tasks per list
-  int pps;          // selected pages per attention task
-  int ns;           // attention tasks per list
-  int n_tasks;
-  int grid;         // workgroups launched: all must be co-resident
+  int chunk_pages;  // pages per chunk task (multiple of 64, <= kStepMaxChunk)
+  int nc;           // chunk tasks per list
+  int n_tasks;      // lists * nc
+  int grid;         // workgroups launched: all co-resident, and >= nc
 };
 
 struct StepArgs {
@@ -45,11 +43,10 @@ struct StepArgs {
   int k_compete, n_head, n_tail;
   float scale_log2;
   float* scores;    // [lists][max_pages]
-  int32_t* sel;     // [lists][max_sel]
-  int32_t* num_sel; // [lists]
-  int32_t* rsel;    // [lists][max_sel] kept pages resolved to (physical << 4) | (valid - 1)
+  int32_t* sel;     // [lists][max_sel], optional
+  int32_t* num_sel; // [lists], optional (given with sel)
   int max_sel;
-  float* partials;  // [lists][ns][G][kHeadDim + 2]
+  float* partials;  // [lists][nc][G][kHeadDim + 2]
   float* out;       // [B][hq][kHeadDim]
   StepCtl* ctl;
   ListCtl* lctl;

@@ -1,29 +1,35 @@
 // sa_step.hip - the whole Quest decode step as one persistent kernel.
 //
 // "SequenceO1" explainer (FlashSA): selection and sparse attention are two
-// stages joined only by integer indices; fusing them into one monolithic
-// kernel cut occupancy.  Here the stages stay separate tasks with their own
-// register/LDS shapes but run inside one launch ("Quest 完全拆解":
-// criticality estimation, top-K filtering, approximate attention; only page
-// numbers cross), so no stage waits for a kernel boundary.
+// stages joined only by integer indices.  "Quest 完全拆解": criticality
+// estimation, top-K filtering, then attention over the kept pages only.
 //
-// Task order: every score chunk (list-major), then every attention split
-// (list-major).  The grid is sized to be co-resident and workgroup w runs
-// tasks w, w + grid, w + 2 grid, ... in order.  A task waits only for tasks
-// earlier in the order; the earliest unfinished task is always running (all
-// workgroups are resident and each runs its tasks in order), so the schedule
-// cannot deadlock.  Hand-offs use device-coherent (sc1) data stores, a wait
-// for their completion, then a relaxed counter:
-//   score chunk -> scores, then score_done[list] += 1; the chunk that brings
-//                  score_done to the chunk count runs the list's top-K at once
-//                  (also resolving the kept pages through the page table) and
-//                  publishes the page lists with sel_ready = 1;
-//   attention   -> waits sel_ready; partial record, then attn_done += 1; the
-//                  split that brings attn_done to the split count merges the
-//                  list's partials into out and clears the list's counters.
-// Every wait is bounded: on timeout ctl.error is set and the kernel still
-// finishes.  Control words live at the head of the caller's workspace: zero
-// before the first call, and every call leaves them zero again.
+// Every list (batch, kv-head) is cut into nc chunks of consecutive logical
+// pages; one task per chunk does, in one workgroup:
+//   1. score its pages (Quest bound) and store the scores, keeping the
+//      chunk's physical page numbers in LDS;
+//   2. publish: score_done[list] += 1, then wait until all nc chunks of the
+//      list have published;
+//   3. run the exact top-K of the whole list from all of its scores -- every
+//      chunk of the list computes the same selection -- and keep only the
+//      selected pages of its own chunk (writing their entries of the optional
+//      page list at their global ranks);
+//   4. attend to those pages (online softmax) and store one partial record;
+//   5. publish: attn_done[list] += 1; the chunk that completes the count
+//      merges the list's nc partials into out and clears the list's counters.
+// So only the scores cross between workgroups before the attention, and the
+// page table is read once per page.
+//
+// Scheduling: task t runs on workgroup t mod grid, in order; every workgroup
+// is co-resident and grid >= nc.  A task waits only for the other chunks of
+// its own list, which sit on other workgroups (nc <= grid); every task of the
+// earliest unfinished list is therefore running or about to run after tasks
+// of finished lists, it publishes its scores before it waits, and so the
+// schedule cannot deadlock.  Hand-offs use device-coherent (sc1) data stores,
+// a wait for their completion, then a relaxed counter update.  Every wait is
+// bounded: on timeout ctl.error is set and the kernel still finishes.  The
+// control words live at the head of the caller's workspace: zero before the
+// first call, and every call leaves them zero again.
 #include "sa_dev_score.h"
 #include "sa_dev_topk.h"
 #include "sa_step.h"
@@ -31,9 +37,10 @@
 namespace sa {
 namespace {
 
-constexpr int kStepThreads = 256;
-constexpr int kScoreIT = 8;               // loads per lane per score pass
-constexpr int kScorePass = 8 * kScoreIT;  // pages per score pass (64)
+constexpr int kStepThreads = 1024;          // one workgroup per CU, 16 waves
+constexpr int kStepWaves = kStepThreads / 64;
+constexpr int kScoreIT = 8;                 // loads per lane per score pass
+constexpr int kScorePass = 2 * kStepWaves * kScoreIT;  // pages per score pass (256)
 constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling (each poll is a memory round trip)
 
 // Thread 0 waits until *p >= target; the workgroup then continues.
@@ -51,7 +58,8 @@ __device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t target
   __syncthreads();
 }
 
-// Every thread's hand-off stores have completed; then thread 0 bumps *ctr.
+// Every thread's hand-off stores have completed; then thread 0 bumps *ctr and
+// gets its old value.
 __device__ __forceinline__ uint32_t publish_add(uint32_t* ctr) {
   stores_done();
   __syncthreads();
@@ -61,67 +69,95 @@ __device__ __forceinline__ uint32_t publish_add(uint32_t* ctr) {
   return old;
 }
 
-template <int KT, int QT, int G>
+template <int G>
 union StepSmem {
   TopkSmem<kStepThreads> topk;
-  AttnSmem<G> attn;
+  AttnSmem<G, kStepWaves> attn;
+  float merge[3 * kStepThreads];
 };
 
 // KPT: top-K keys per thread in registers (lists of up to 256 * KPT pages).
 template <int KT, int QT, int G, int KPT>
-__global__ __launch_bounds__(kStepThreads, 4) void quest_step_kernel(StepArgs A, StepPlan P) {
-  __shared__ StepSmem<KT, QT, G> sm;
-  __shared__ int s_flag;
-  const int tid = threadIdx.x;
+__global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A, StepPlan P) {
+  __shared__ StepSmem<G> sm;
+  __shared__ int32_t s_pp[kStepMaxChunk];    // physical page of each chunk page, or -1
+  __shared__ int32_t s_kept[kStepMaxChunk];  // chunk page kept by the selection
+  __shared__ int32_t s_list[kStepMaxChunk];  // kept pages: (physical << 4) | (valid - 1)
+  __shared__ int s_cnt, s_flag;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = A.hkv * G;
-  const int n_score = P.lists * P.nc;
 
   for (int t = blockIdx.x; t < P.n_tasks; t += gridDim.x) {
-    const bool scoring = t < n_score;
-    const int i = scoring ? t / P.nc : (t - n_score) / P.ns;
-    const int idx = scoring ? t % P.nc : (t - n_score) % P.ns;
+    const int i = t / P.nc, c = t % P.nc;
     const int b = i / A.hkv, h = i % A.hkv;
     ListCtl* lc = A.lctl + i;
-    const int L = clamp_len(A.lens[b], A.max_pages);
-    const int n = (L + kPage - 1) / kPage;
     const int32_t* pt_row = A.pt + (size_t)b * A.max_pages;
+    const int c0 = c * P.chunk_pages;
+    float* sc_row = A.scores + (size_t)i * A.max_pages;
 
-    if (scoring) {  // ------------------------------------- score chunk (+ top-K)
-      const int c0 = idx * P.chunk_pages;
-      const int c1 = min(c0 + P.chunk_pages, n);
-      float* sc_row = A.scores + (size_t)i * A.max_pages;
-      for (int p0 = c0; p0 < c1; p0 += kScorePass)
-        quest_score_range<KT, QT, G, kScoreIT, true>(A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row,
-                                                     p0, min(p0 + kScorePass, c1), sc_row);
-      const uint32_t old = publish_add(&lc->score_done);
-      if (tid == 0) s_flag = old == (uint32_t)(P.nc - 1);
-      __syncthreads();
-      if (s_flag) {  // the list's last chunk: every score is in, select now
-        topk_list<kStepThreads, KPT, true>(sc_row, n, n, 1, A.k_compete, A.n_head, A.n_tail,
-                                                A.sel + (size_t)i * A.max_sel, A.num_sel + i,
-                                                A.max_sel, sm.topk, pt_row, L, A.num_pages,
-                                                A.rsel + (size_t)i * A.max_sel);
-        publish_add(&lc->sel_ready);
-      }
-    } else {  // -------------------------------------------------------- attention split
-      wait_at_least(&lc->sel_ready, 1u, &A.ctl->error);
-      const int cnt = min(ld_x<true>(A.num_sel + i), A.max_sel);
-      const int j0 = idx * P.pps, j1 = min(j0 + P.pps, cnt);
-      float* part_list = A.partials + (size_t)i * P.ns * G * kPartStride;
-      attend_range<KT, QT, G, 1, true>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
-                                       pt_row, L, A.sel + (size_t)i * A.max_sel, j0, j1,
-                                       A.scale_log2, part_list + (size_t)idx * G * kPartStride,
-                                       sm.attn, A.rsel + (size_t)i * A.max_sel);
-      const uint32_t old = publish_add(&lc->attn_done);
-      if (tid == 0) s_flag = old == (uint32_t)(P.ns - 1);
-      __syncthreads();
-      if (s_flag) {
-        merge_list<true>(part_list, P.ns, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim);
-        if (tid == 0) {  // every task of this list has finished: clear its counters
-          st_x<true>(&lc->score_done, 0u);
-          st_x<true>(&lc->sel_ready, 0u);
-          st_x<true>(&lc->attn_done, 0u);
+    // 1. scores of the chunk; the passes cover the chunk up to the page-table
+    // row length, so their loads need not wait for the sequence length
+    const int c_end = min(c0 + P.chunk_pages, A.max_pages);
+    int n = 0;
+    for (int p0 = c0; p0 < c_end; p0 += kScorePass)
+      n = quest_score_range<KT, QT, G, kScoreIT, true, kStepWaves>(A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row,
+                                                       p0, min(p0 + kScorePass, c_end), A.lens + b,
+                                                       A.max_pages, sc_row, s_pp + (p0 - c0));
+    const int L = clamp_len(A.lens[b], A.max_pages);
+    if (c0 >= c_end) n = (L + kPage - 1) / kPage;
+    const int c1 = min(c0 + P.chunk_pages, n);  // c1 <= c0: an empty chunk
+    for (int j = tid; j < P.chunk_pages; j += kStepThreads) s_kept[j] = 0;
+    // 2. publish, then wait for the list's other chunks
+    publish_add(&lc->score_done);
+    wait_at_least(&lc->score_done, (uint32_t)P.nc, &A.ctl->error);
+
+    // 3. the list's selection; keep this chunk's part
+    int32_t* sel_row = A.sel ? A.sel + (size_t)i * A.max_sel : nullptr;
+    topk_core<kStepThreads, KPT, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
+                                       [&](int rank, int u) {
+                                         if (u >= c0 && u < c1) {
+                                           s_kept[u - c0] = 1;
+                                           if (sel_row && rank < A.max_sel) sel_row[rank] = u;
+                                         }
+                                       });
+    if (sel_row && c == 0) {  // count and padding of the optional page list
+      const int cnt = min(min(n, A.n_head + A.k_compete + A.n_tail), A.max_sel);
+      for (int j = cnt + tid; j < A.max_sel; j += kStepThreads) sel_row[j] = -1;
+      if (tid == 0) A.num_sel[i] = cnt;
+    }
+    __syncthreads();
+    if (wave == 0) {  // kept pages of the chunk, ascending, resolved through the page table
+      int cnt = 0;
+      for (int base = 0; base < c1 - c0; base += 64) {
+        const int j = base + lane;
+        const int pp = j < c1 - c0 ? s_pp[j] : -1;
+        const bool kf = j < c1 - c0 && s_kept[j] != 0 && pp >= 0;
+        const uint64_t bal = __ballot(kf);
+        if (kf) {
+          const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
+          s_list[pos] = (pp << 4) | (min(kPage, L - (c0 + j) * kPage) - 1);
         }
+        cnt += __popcll(bal);
+      }
+      if (lane == 0) s_cnt = cnt;
+    }
+    __syncthreads();
+
+    // 4. attention over the chunk's kept pages
+    float* part_list = A.partials + (size_t)i * P.nc * G * kPartStride;
+    attend_range<KT, QT, G, 1, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
+                                     pt_row, L, nullptr, 0, s_cnt, A.scale_log2,
+                                     part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
+    // 5. publish; the list's last chunk merges
+    const uint32_t old = publish_add(&lc->attn_done);
+    if (tid == 0) s_flag = old == (uint32_t)(P.nc - 1);
+    __syncthreads();
+    if (s_flag) {
+      merge_list<true>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim,
+                       sm.merge);
+      if (tid == 0) {  // every chunk of this list has finished: clear its counters
+        st_x<true>(&lc->score_done, 0u);
+        st_x<true>(&lc->attn_done, 0u);
       }
     }
     __syncthreads();  // shared memory and s_flag are reused by the next task
@@ -130,19 +166,19 @@ __global__ __launch_bounds__(kStepThreads, 4) void quest_step_kernel(StepArgs A,
 
 template <int KT, int QT>
 hipError_t step_dispatch(int kpt, const StepArgs& A, const StepPlan& P, hipStream_t st) {
-  if (kpt <= 8)
-    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 8>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
+  if (kpt <= 2)
+    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 2>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
   else
-    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 16>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
+    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 4>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
   return hipGetLastError();
 }
 
 template <int KT, int QT>
 int resident_of(int kpt) {
   int per_cu = 0;
-  const hipError_t e = kpt <= 8
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 8>, kStepThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 16>, kStepThreads, 0);
+  const hipError_t e = kpt <= 2
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 2>, kStepThreads, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 4>, kStepThreads, 0);
   return e == hipSuccess ? per_cu : 0;
 }
 
@@ -150,29 +186,26 @@ int resident_of(int kpt) {
 
 StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_cus) {
   StepPlan P{};
+  (void)Hq;
+  (void)max_sel;
   P.lists = B * Hkv;
   const long lists = P.lists;
-  (void)Hq;
-  const long wgs = (long)num_cus * 4;  // resident workgroups aimed for
-  // score chunks: about one per resident workgroup overall, whole passes of 64 pages
+  const long wgs = num_cus;  // resident workgroups aimed for: one per CU
+  // chunks: about one per resident workgroup overall, whole score passes
   long chunk = (lists * max_pages + wgs - 1) / wgs;
   chunk = (chunk + kScorePass - 1) / kScorePass * kScorePass;
   if (chunk < kScorePass) chunk = kScorePass;
+  if (chunk > kStepMaxChunk) chunk = kStepMaxChunk;
   P.chunk_pages = (int)chunk;
   P.nc = (int)((max_pages + chunk - 1) / chunk);
-  // attention splits: about one per resident workgroup, >= 4 pages (one per wave)
-  long pps = (lists * max_sel + wgs - 1) / wgs;
-  if (pps < 4) pps = 4;
-  P.pps = (int)pps;
-  P.ns = (int)((max_sel + pps - 1) / pps);
-  P.n_tasks = (int)(lists * (P.nc + P.ns));
+  P.n_tasks = (int)(lists * P.nc);
   P.grid = (int)(wgs < P.n_tasks ? wgs : P.n_tasks);
   return P;
 }
 
 size_t step_ctl_bytes(int lists) { return sizeof(StepCtl) + (size_t)lists * sizeof(ListCtl); }
 
-int step_kpt(int max_pages) { return max_pages <= kStepThreads * 8 ? 8 : 16; }
+int step_kpt(int max_pages) { return max_pages <= kStepThreads * 2 ? 2 : 4; }
 
 int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus) {
   int per_cu;
