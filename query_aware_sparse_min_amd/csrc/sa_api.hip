@@ -118,7 +118,7 @@ int resident_step_wgs(int kv_dtype, int q_dtype, int max_pages) {
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   const int kpt = step_kpt(max_pages);
-  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1) + (kpt > 2 ? 4 : 0);
+  const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1) + (kpt > step_kpt(1) ? 4 : 0);
   if (dev < 64) {
     const int c = cache[dev][slot].load(std::memory_order_relaxed);
     if (c > 0) return c;

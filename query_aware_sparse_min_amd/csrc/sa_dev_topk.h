@@ -36,11 +36,18 @@ namespace sa {
 constexpr int kTopkDigit = 8;
 constexpr int kTopkBins = 1 << kTopkDigit;
 
+constexpr int kTopkCand = 64;  // threshold bins this small are resolved by one wave
+
 template <int NT>
 struct TopkSmem {
   alignas(16) uint32_t hist[3][kTopkBins];
   uint32_t wmin[NT / 64], wmax[NT / 64];
   uint32_t wa[NT / 64], wb[NT / 64];
+  // keys of the threshold bin: (key << 32) | ~unit, so that a larger value is
+  // the better unit under (key desc, unit asc)
+  unsigned long long cand[kTopkCand];
+  int32_t ckept[kTopkCand];
+  int ncand;
   int last_kept;
 };
 
@@ -51,19 +58,21 @@ __device__ __forceinline__ uint32_t order_key(float f) {
 }
 
 // Selection core of one list.  sc: the list's n unit scores.  Calls
-// keep(rank, u) exactly once for every kept unit u, where rank is u's position
-// among the kept units in ascending unit order (any thread may make a call).
-// KPT > 0 requires n - n_head - n_tail <= NT * KPT.  COH: the scores are read
-// device-coherently.  All NT threads call; sm is free again on return once the
-// caller has synchronised.
+// keep(rank, u) exactly once for every kept unit u (any thread may make a
+// call).  With want_rank, rank is u's position among the kept units in
+// ascending unit order; otherwise it is -1 and the ranking scan is skipped
+// unless exact ties need it.  KPT > 0 requires n - n_head - n_tail <= NT * KPT.
+// COH: the scores are read device-coherently.  All NT threads call; sm is free
+// again on return once the caller has synchronised.
 template <int NT, int KPT, bool COH, typename Keep>
 __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, int k, int n_head,
-                                          int n_tail, TopkSmem<NT>& sm, Keep&& keep) {
+                                          int n_tail, TopkSmem<NT>& sm, Keep&& keep,
+                                          bool want_rank = true) {
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
   if (n <= n_head + n_tail + k) {  // every unit is kept; no padding
-    for (int u = tid; u < n; u += NT) keep(u, u);
+    for (int u = tid; u < n; u += NT) keep(want_rank ? u : -1, u);
     return;
   }
   const int m = n - n_head - n_tail;  // competing middle units; m > k >= 0
@@ -98,9 +107,12 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   };
 
   for (int i = tid; i < 3 * kTopkBins; i += NT) (&sm.hist[0][0])[i] = 0u;
+  if (tid == 0) sm.ncand = 0;
 
-  // threshold: keys whose bits under mask dm equal tval; rem of them are kept
-  uint32_t dm = 0xFFFFFFFFu, tval = 0xFFFFFFFFu, rem = 0;
+  // threshold: keys whose bits under mask dm equal tval ("at" keys, cbin of
+  // them); rem of them are kept, every key above is kept
+  uint32_t dm = 0xFFFFFFFFu, tval = 0xFFFFFFFFu, rem = 0, cbin = 0;
+  bool cand = false;  // the at keys are few: one wave ranks them exactly
   if (k > 0) {
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for_keys([&](int, uint32_t x) { kmin = min(kmin, x); kmax = max(kmax, x); });
@@ -113,6 +125,7 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
     rem = (uint32_t)k;
     const uint32_t diff = kmin ^ kmax;
     tval = kmax;
+    cbin = (uint32_t)m;  // all keys are equal when diff == 0
     if (diff != 0u) {
       int nb = 32 - __clz(diff);  // low bits still undetermined
       dm = nb >= 32 ? 0u : 0xFFFFFFFFu << nb;
@@ -139,7 +152,8 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
         const uint64_t hit = __ballot(before < rem && rem <= incl);  // exactly one lane
         const int src = __ffsll((unsigned long long)hit) - 1;
         int bin = 0;
-        uint32_t cbin = 0, nrem = 0;
+        uint32_t nrem = 0;
+        cbin = 0;
         const uint32_t c4[4] = {hv.w, hv.z, hv.y, hv.x};
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
@@ -157,33 +171,93 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
         dm |= dmask << shift;
         nb = shift;
         if (nb == 0 || cbin == rem) break;  // fully determined, or the whole bin is kept
+        if (cbin <= (uint32_t)kTopkCand) {
+          cand = true;
+          break;
+        }
       }
     }
+    if (!cand && cbin != rem && cbin <= (uint32_t)kTopkCand) cand = true;  // exact ties, few
   }
-
-  // rank the kept middle units in index order: one block scan of (#above, #at) the threshold
-  uint32_t gt = 0, eq = 0;
-  if (k > 0) for_keys([&](int, uint32_t x) { gt += (x & dm) > tval; eq += (x & dm) == tval; });
-  const uint32_t ga = wave_incl_scan_u32(gt), ea = wave_incl_scan_u32(eq);
-  if (lane == 63) { sm.wa[wave] = ga; sm.wb[wave] = ea; }
-  __syncthreads();
-  uint32_t gt_before = ga - gt, eq_before = ea - eq;
-#pragma unroll
-  for (int w2 = 0; w2 < NW; ++w2)
-    if (w2 < wave) { gt_before += sm.wa[w2]; eq_before += sm.wb[w2]; }
-
-  if (k > 0) {
-    uint32_t kept_before = gt_before + min(eq_before, rem);
-    uint32_t eq_seen = eq_before;
+  int cslot[KPT > 0 ? KPT : 1];  // candidate slot of each register key
+  if (cand) {
+    // gather the at keys, rank them by (key desc, unit asc) in one wave, mark the kept
     for_keys([&](int j, uint32_t x) {
+      if ((x & dm) == tval) {
+        const int slot = atomicAdd(&sm.ncand, 1);
+        sm.cand[slot] = ((unsigned long long)x << 32) | (uint32_t)~(uint32_t)(n_head + r0 + j);
+        if constexpr (KPT > 0) cslot[j] = slot;
+      }
+    });
+    __syncthreads();
+    if (wave == 0) {  // lane i ranks candidate i against all (LDS broadcast reads)
+      const int nc = __builtin_amdgcn_readfirstlane((int)cbin);
+      const unsigned long long me = sm.cand[lane < nc ? lane : 0];
+      uint32_t rk = 0;
+      for (int j0 = 0; j0 < nc; j0 += 16) {
+#pragma unroll
+        for (int j = j0; j < j0 + 16; ++j) {  // unconditional reads, one compare each
+          const unsigned long long o = sm.cand[j];  // entries >= nc are stale: masked below
+          rk += (uint32_t)(o > me) & (uint32_t)(j < nc);
+        }
+      }
+      if (lane < nc) sm.ckept[lane] = rk < rem ? 1 : 0;
+    }
+    __syncthreads();
+  }
+  // is the at key j of this thread kept?  (only asked when cand)
+  auto cand_kept = [&](int j) -> bool {
+    if constexpr (KPT > 0) {
+      return sm.ckept[cslot[j]] != 0;
+    } else {  // keys re-read: find the unit among the candidates
+      const int u = n_head + r0 + j, nc = (int)cbin;
+      bool r = false;
+      for (int s2 = 0; s2 < nc; ++s2)
+        if ((uint32_t)~(uint32_t)sm.cand[s2] == (uint32_t)u) r = sm.ckept[s2] != 0;
+      return r;
+    }
+  };
+
+  // At keys are kept by the candidate ranks (cand), all of them (cbin == rem),
+  // or else the first rem in unit order, which needs a block scan of the at
+  // keys; the output ranks need a block scan of the kept keys.
+  const bool tie_scan = k > 0 && !cand && cbin != rem;
+  const bool scan = k > 0 && (tie_scan || want_rank);
+  uint32_t kept_before = 0, eq_seen = 0;
+  if (scan) {
+    uint32_t gt = 0, eq = 0;
+    for_keys([&](int j, uint32_t x) {
+      const uint32_t xm = x & dm;
+      gt += xm > tval;
+      if (xm == tval) eq += (!cand || cand_kept(j)) ? 1u : 0u;
+    });
+    const uint32_t ga = wave_incl_scan_u32(gt), ea = wave_incl_scan_u32(eq);
+    if (lane == 63) { sm.wa[wave] = ga; sm.wb[wave] = ea; }
+    __syncthreads();
+    uint32_t gt_before = ga - gt, eq_before = ea - eq;
+#pragma unroll
+    for (int w2 = 0; w2 < NW; ++w2)
+      if (w2 < wave) { gt_before += sm.wa[w2]; eq_before += sm.wb[w2]; }
+    kept_before = gt_before + (tie_scan ? min(eq_before, rem) : eq_before);
+    eq_seen = eq_before;
+  }
+  if (k > 0) {
+    for_keys([&](int j, uint32_t x) {
+      const int u = n_head + r0 + j;
       const uint32_t xm = x & dm;
       bool kp = xm > tval;
       if (xm == tval) {
-        kp = eq_seen < rem;
-        ++eq_seen;
+        if (cand) {
+          kp = cand_kept(j);
+        } else if (tie_scan) {
+          kp = eq_seen < rem;
+          ++eq_seen;
+        } else {
+          kp = true;
+        }
       }
       if (kp) {
-        keep(n_head + (int)kept_before, n_head + r0 + j);
+        keep(scan && want_rank ? n_head + (int)kept_before : -1, u);
         ++kept_before;
       }
     });
@@ -191,7 +265,8 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   // forced units: c < n_head is head unit c (rank c); else tail unit n - n_tail + j (rank n_head + k + j)
   for (int c = tid; c < n_head + n_tail; c += NT) {
     const bool head = c < n_head;
-    keep(head ? c : n_head + k + (c - n_head), head ? c : n - n_tail + (c - n_head));
+    const int rank = head ? c : n_head + k + (c - n_head);
+    keep(want_rank ? rank : -1, head ? c : n - n_tail + (c - n_head));
   }
 }
 

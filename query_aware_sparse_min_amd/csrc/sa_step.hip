@@ -37,10 +37,11 @@
 namespace sa {
 namespace {
 
-constexpr int kStepThreads = 1024;          // one workgroup per CU, 16 waves
-constexpr int kStepWaves = kStepThreads / 64;
-constexpr int kScoreIT = 8;                 // loads per lane per score pass
-constexpr int kScorePass = 2 * kStepWaves * kScoreIT;  // pages per score pass (256)
+constexpr int kStepWaves = 12;              // one workgroup per CU: 12 waves, 168 VGPRs each
+constexpr int kStepThreads = 64 * kStepWaves;
+constexpr int kScoreIT = (128 + kStepWaves - 1) / kStepWaves;  // loads per lane per score pass
+constexpr int kScorePass = 2 * kStepWaves * kScoreIT;           // pages per score pass (>= 256)
+constexpr int kStepChunkCap = kStepMaxChunk / kScorePass * kScorePass;
 constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling (each poll is a memory round trip)
 
 // Thread 0 waits until *p >= target; the workgroup then continues.
@@ -119,7 +120,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
                                            s_kept[u - c0] = 1;
                                            if (sel_row && rank < A.max_sel) sel_row[rank] = u;
                                          }
-                                       });
+                                       }, sel_row != nullptr);
     if (sel_row && c == 0) {  // count and padding of the optional page list
       const int cnt = min(min(n, A.n_head + A.k_compete + A.n_tail), A.max_sel);
       for (int j = cnt + tid; j < A.max_sel; j += kStepThreads) sel_row[j] = -1;
@@ -164,21 +165,25 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
   }
 }
 
+// register-resident top-K keys per thread: lists of up to kStepThreads * kKptLo pages, else kKptHi
+constexpr int kKptLo = (2048 + kStepThreads - 1) / kStepThreads;
+constexpr int kKptHi = (kStepMaxPages + kStepThreads - 1) / kStepThreads;
+
 template <int KT, int QT>
 hipError_t step_dispatch(int kpt, const StepArgs& A, const StepPlan& P, hipStream_t st) {
-  if (kpt <= 2)
-    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 2>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
+  if (kpt <= kKptLo)
+    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, kKptLo>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
   else
-    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, 4>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
+    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, kKptHi>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
   return hipGetLastError();
 }
 
 template <int KT, int QT>
 int resident_of(int kpt) {
   int per_cu = 0;
-  const hipError_t e = kpt <= 2
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 2>, kStepThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, 4>, kStepThreads, 0);
+  const hipError_t e = kpt <= kKptLo
+      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, kKptLo>, kStepThreads, 0)
+      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, kKptHi>, kStepThreads, 0);
   return e == hipSuccess ? per_cu : 0;
 }
 
@@ -195,7 +200,7 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
   long chunk = (lists * max_pages + wgs - 1) / wgs;
   chunk = (chunk + kScorePass - 1) / kScorePass * kScorePass;
   if (chunk < kScorePass) chunk = kScorePass;
-  if (chunk > kStepMaxChunk) chunk = kStepMaxChunk;
+  if (chunk > kStepChunkCap) chunk = kStepChunkCap;
   P.chunk_pages = (int)chunk;
   P.nc = (int)((max_pages + chunk - 1) / chunk);
   P.n_tasks = (int)(lists * P.nc);
@@ -205,7 +210,7 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
 
 size_t step_ctl_bytes(int lists) { return sizeof(StepCtl) + (size_t)lists * sizeof(ListCtl); }
 
-int step_kpt(int max_pages) { return max_pages <= kStepThreads * 2 ? 2 : 4; }
+int step_kpt(int max_pages) { return max_pages <= kStepThreads * kKptLo ? kKptLo : kKptHi; }
 
 int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus) {
   int per_cu;
