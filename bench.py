@@ -27,6 +27,23 @@ sys.path.insert(0, ROOT)
 
 METRIC = "sparse decode-step µs + effective HBM GB/s (% of peak), 32K ctx, 2048-token budget"
 PEAK_GBS = 8000.0  # MI355X HBM3E
+STEP_KERNEL = "quest_step_kernel"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "quest_step_kernel_llama7b_32k_traffic.json")
+CALIB_BYTES = 256 << 20  # the plain copy timed beside the step in a counter run
+# sources the fused step kernel is compiled from: counters taken on other sources are stale
+KERNEL_SOURCES = ["include/sa.h"] + [
+    "query_aware_sparse_min_amd/csrc/" + f
+    for f in ("sa_step.hip", "sa_step.h", "sa_dev_score.h", "sa_dev_topk.h", "sa_dev_attn.h",
+              "sa_internal.h")]
+
+
+def kernel_source_hash():
+    import hashlib
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
 
 
 def parse():
@@ -37,11 +54,65 @@ def parse():
     ap.add_argument("--copies", type=int, default=16, help="layer copies rotated per step")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
+    ap.add_argument("--pmc-run", action="store_true",
+                    help="run a few steps and a plain copy of known size, for a counter run")
+    ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
+                    help="write the HBM traffic record from two rocprofv3 --pmc outputs")
     return ap.parse_args()
+
+
+def parse_pmc(fetch_csv, write_csv):
+    """HBM bytes per step-kernel launch from rocprofv3 counter files (FETCH_SIZE,
+    WRITE_SIZE in KiB per dispatch), each scaled by what the same counter reads
+    for the plain copy of CALIB_BYTES that the counter run also launches."""
+    import csv
+    import json
+
+    def per_kernel(path, counter):
+        """(step-kernel values, value of the last copy dispatch) in bytes."""
+        step, copies = [], []
+        with open(path) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") != counter:
+                    continue
+                v = float(r["Counter_Value"]) * 1024.0
+                if STEP_KERNEL in r["Kernel_Name"]:
+                    step.append(v)
+                elif "copy" in r["Kernel_Name"].lower():
+                    copies.append((int(r["Dispatch_Id"]), v))
+        return step, max(copies)[1]  # the calibration copy is the last copy dispatched
+
+    fs, fc = per_kernel(fetch_csv, "FETCH_SIZE")
+    ws, wc = per_kernel(write_csv, "WRITE_SIZE")
+    fk, wk = sum(fs) / len(fs), sum(ws) / len(ws)
+    rec = {"kernel": STEP_KERNEL, "kernel_src_sha": kernel_source_hash(),
+           "fetch_bytes_raw": round(fk), "write_bytes_raw": round(wk),
+           "copy_bytes": CALIB_BYTES, "copy_fetch_raw": round(fc), "copy_write_raw": round(wc),
+           "fetch_scale": CALIB_BYTES / fc, "write_scale": CALIB_BYTES / wc,
+           "fetch_bytes": round(fk * CALIB_BYTES / fc), "write_bytes": round(wk * CALIB_BYTES / wc)}
+    rec["traffic_bytes"] = rec["fetch_bytes"] + rec["write_bytes"]
+    os.makedirs(os.path.dirname(TRAFFIC_FILE), exist_ok=True)
+    with open(TRAFFIC_FILE, "w") as fh:
+        json.dump(rec, fh, indent=1)
+    print(json.dumps(rec))
+
+
+def load_traffic():
+    """Counter-measured bytes per launch, or None when absent or taken on other sources."""
+    import json
+    try:
+        with open(TRAFFIC_FILE) as fh:
+            rec = json.load(fh)
+    except (OSError, ValueError):
+        return None
+    return rec.get("traffic_bytes") if rec.get("kernel_src_sha") == kernel_source_hash() else None
 
 
 def main():
     args = parse()
+    if args.parse_pmc:
+        parse_pmc(*args.parse_pmc)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(this path has no multi-GPU part)", file=sys.stderr)
@@ -85,6 +156,20 @@ def main():
     def step(i):
         kv, meta = copies[i % R]
         sa.sa_decode_step(qs[i % NQ], kv, seqs, cfg, meta, None, wl.softmax_scale, out, ws)
+
+    if args.pmc_run:  # a few eager steps on cold copies, then the calibration copy
+        for i in range(args.warmup):
+            step(i)
+        torch.cuda.synchronize()
+        for i in range(4):
+            step(args.warmup + i)
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        print("pmc run done", flush=True)
+        return
 
     stream = torch.cuda.current_stream()
     for i in range(args.warmup):
@@ -206,7 +291,7 @@ def main():
                                      "sparse_decode_attn": round(attn_us, 2)},
         "roofline": {"bound": "hbm", "kernel": dom_name, "achieved": round(dom_gbs, 1),
                      "peak": PEAK_GBS, "unit": "GB/s", "frac": round(dom_gbs / PEAK_GBS, 4),
-                     "traffic": None},
+                     "traffic": load_traffic()},
         "cpu_baseline": cpu,
         "setup_s": round(setup_s, 1),
     }
