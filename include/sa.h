@@ -221,11 +221,12 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  * skipped and dense attention runs.  sel / num_sel (optional, may be NULL)
  * receive the selection as sa_topk_pages writes it.
  * Quest mode with one query head per kv-head runs as a single persistent
- * kernel whose workgroups hand work to each other through control words at
- * the head of the workspace: the workspace must be zero-filled before its
- * first use, every call leaves those words zero again, and one workspace
- * serves one call at a time.  A bounded wait that times out (never expected)
- * sets the 32-bit word at byte offset 8 of the workspace to nonzero.
+ * kernel whose workgroups hand work to each other through the workspace
+ * (control words, score keys, partial records, where 0 means "not written
+ * yet"): the workspace must be zero-filled before its first use, every call
+ * leaves those words zero again, and one workspace serves one call at a time.
+ * A bounded wait that times out (never expected) sets the 32-bit word at byte
+ * offset 8 of the workspace to nonzero.
  */
 int sa_decode_step(const void *q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache *kv,
                    const sa_seqs *seqs, const sa_select_cfg *cfg, const void *meta,

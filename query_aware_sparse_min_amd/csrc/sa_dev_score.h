@@ -21,10 +21,11 @@ namespace sa {
 // n is ceil(min(*len_b, 16 max_pages) / 16), read after the page-table and
 // metadata loads have been issued so that they need not wait for it; the
 // function returns n.  sc_row: the list's scores (device-coherent stores when
-// COH).  pp_out (optional, LDS): the physical page of page p0 + j at [j], -1
+// COH; KEYS: stored as order_key() words instead of floats).  pp_out
+// (optional, LDS): the physical page of page p0 + j at [j], -1
 // when the page is invalid or its page-table entry is out of range.  All
 // 64 * NW threads call.
-template <int KT, int QT, int G, int IT, bool COH = false, int NW = 4>
+template <int KT, int QT, int G, int IT, bool COH = false, int NW = 4, bool KEYS = false>
 __device__ __forceinline__ int quest_score_range(const void* __restrict__ q,
                                                   const void* __restrict__ meta, int num_pages,
                                                   int hkv, int b, int h,
@@ -80,7 +81,9 @@ __device__ __forceinline__ int quest_score_range(const void* __restrict__ q,
       best = fmaxf(best, s);
     }
     if ((lane & 31) == 0 && pg[it] < p1) {
-      st_x<COH>(sc_row + pg[it], ok ? best : -INFINITY);
+      const float sv = ok ? best : -INFINITY;
+      if constexpr (KEYS) st_x<COH>(reinterpret_cast<uint32_t*>(sc_row) + pg[it], order_key(sv));
+      else st_x<COH>(sc_row + pg[it], sv);
       if (pp_out) pp_out[pg[it] - p0] = ok ? ppg[it] : -1;
     }
   }

@@ -46,28 +46,25 @@ struct TopkSmem {
   // keys of the threshold bin: (key << 32) | ~unit, so that a larger value is
   // the better unit under (key desc, unit asc)
   unsigned long long cand[kTopkCand];
-  int32_t ckept[kTopkCand];
+  uint32_t crank[kTopkCand];  // number of better candidates
   int ncand;
   int last_kept;
 };
-
-__device__ __forceinline__ uint32_t order_key(float f) {
-  f = f + 0.0f;  // -0.0 -> +0.0
-  const uint32_t u = __float_as_uint(f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-}
 
 // Selection core of one list.  sc: the list's n unit scores.  Calls
 // keep(rank, u) exactly once for every kept unit u (any thread may make a
 // call).  With want_rank, rank is u's position among the kept units in
 // ascending unit order; otherwise it is -1 and the ranking scan is skipped
 // unless exact ties need it.  KPT > 0 requires n - n_head - n_tail <= NT * KPT.
-// COH: the scores are read device-coherently.  All NT threads call; sm is free
-// again on return once the caller has synchronised.
-template <int NT, int KPT, bool COH, typename Keep>
+// COH: the scores are read device-coherently.  KEYS (KPT > 0 only): sc holds
+// order_key() words written by other workgroups, 0 while not yet written; such
+// words are re-read until they arrive (bounded; on timeout *err |= 2).  All NT
+// threads call; sm is free again on return once the caller has synchronised.
+template <int NT, int KPT, bool COH, bool KEYS = false, typename Keep>
 __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, int k, int n_head,
                                           int n_tail, TopkSmem<NT>& sm, Keep&& keep,
-                                          bool want_rank = true) {
+                                          bool want_rank = true, uint32_t* err = nullptr) {
+  static_assert(!KEYS || KPT > 0, "key hand-off needs register-resident keys");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
@@ -85,7 +82,31 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   // in-range indices so that they are all in flight together; out-of-run
   // values are discarded afterwards.
   uint32_t key[KPT > 0 ? KPT : 1];
-  if constexpr (KPT > 0) {
+  if constexpr (KEYS) {
+    const uint32_t* mk = reinterpret_cast<const uint32_t*>(sc) + n_head;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = ld_x<true>(mk + min(r0 + j, m - 1));
+    bool missing = false;
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) missing |= j < cnt_t && key[j] == 0u;
+    for (uint32_t spins = 0; missing; ++spins) {  // stores not yet landed: re-read those words
+      if (spins > kPollLimit) {
+        if (err) __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        break;
+      }
+      __builtin_amdgcn_s_sleep(1);
+      missing = false;
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) {
+        if (j < cnt_t && key[j] == 0u) {
+          key[j] = ld_x<true>(mk + r0 + j);
+          missing |= key[j] == 0u;
+        }
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? key[j] : 0u;
+  } else if constexpr (KPT > 0) {
     float v[KPT];
 #pragma unroll
     for (int j = 0; j < KPT; ++j) v[j] = ld_x<COH>(msc + min(r0 + j, m - 1));
@@ -107,6 +128,7 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   };
 
   for (int i = tid; i < 3 * kTopkBins; i += NT) (&sm.hist[0][0])[i] = 0u;
+  for (int i = tid; i < kTopkCand; i += NT) sm.crank[i] = 0u;
   if (tid == 0) sm.ncand = 0;
 
   // threshold: keys whose bits under mask dm equal tval ("at" keys, cbin of
@@ -181,7 +203,8 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   }
   int cslot[KPT > 0 ? KPT : 1];  // candidate slot of each register key
   if (cand) {
-    // gather the at keys, rank them by (key desc, unit asc) in one wave, mark the kept
+    // gather the at keys and rank them by (key desc, unit asc): lane i of wave w
+    // counts the candidates of the w-th slice that beat candidate i
     for_keys([&](int j, uint32_t x) {
       if ((x & dm) == tval) {
         const int slot = atomicAdd(&sm.ncand, 1);
@@ -190,30 +213,28 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
       }
     });
     __syncthreads();
-    if (wave == 0) {  // lane i ranks candidate i against all (LDS broadcast reads)
+    {
       const int nc = __builtin_amdgcn_readfirstlane((int)cbin);
-      const unsigned long long me = sm.cand[lane < nc ? lane : 0];
-      uint32_t rk = 0;
-      for (int j0 = 0; j0 < nc; j0 += 16) {
-#pragma unroll
-        for (int j = j0; j < j0 + 16; ++j) {  // unconditional reads, one compare each
-          const unsigned long long o = sm.cand[j];  // entries >= nc are stale: masked below
-          rk += (uint32_t)(o > me) & (uint32_t)(j < nc);
-        }
+      const int per = (nc + NW - 1) / NW;
+      const int j0 = wave * per, j1 = min(nc, j0 + per);
+      if (lane < nc && j0 < j1) {
+        const unsigned long long me = sm.cand[lane];
+        uint32_t rk = 0;
+        for (int j = j0; j < j1; ++j) rk += sm.cand[j] > me ? 1u : 0u;
+        if (rk) atomicAdd(&sm.crank[lane], rk);
       }
-      if (lane < nc) sm.ckept[lane] = rk < rem ? 1 : 0;
     }
     __syncthreads();
   }
   // is the at key j of this thread kept?  (only asked when cand)
   auto cand_kept = [&](int j) -> bool {
     if constexpr (KPT > 0) {
-      return sm.ckept[cslot[j]] != 0;
+      return sm.crank[cslot[j]] < rem;
     } else {  // keys re-read: find the unit among the candidates
       const int u = n_head + r0 + j, nc = (int)cbin;
       bool r = false;
       for (int s2 = 0; s2 < nc; ++s2)
-        if ((uint32_t)~(uint32_t)sm.cand[s2] == (uint32_t)u) r = sm.ckept[s2] != 0;
+        if ((uint32_t)~(uint32_t)sm.cand[s2] == (uint32_t)u) r = sm.crank[s2] < rem;
       return r;
     }
   };

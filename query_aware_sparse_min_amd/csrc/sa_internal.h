@@ -145,6 +145,20 @@ __device__ __forceinline__ void st_x(T* p, T v) {
   if constexpr (COH) __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
   else *p = v;
 }
+// Order-preserving unsigned key of a score (-0.0 folded into +0.0).  Never 0
+// for a non-NaN score, so 0 can mark a key that has not been written yet.
+__device__ __forceinline__ uint32_t order_key(float f) {
+  f = f + 0.0f;  // -0.0 -> +0.0
+  const uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+// Partial records handed between workgroups are stored as (bits ^ kPartSentinel):
+// the sentinel is a NaN payload no partial value takes, so a zero word is one
+// that has not been written yet, and zero-filled memory reads as "absent".
+constexpr uint32_t kPartSentinel = 0x7FC0DEADu;
+constexpr uint32_t kPollLimit = 1u << 18;  // bounded re-polls of a not-yet-written word
+
 // Wait until this thread's stores have completed (s_waitcnt vmcnt(0)); the
 // signal fences keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void stores_done() {

@@ -6,7 +6,7 @@
 //
 // Every list (batch, kv-head) is cut into nc chunks of consecutive logical
 // pages; one task per chunk does, in one workgroup:
-//   1. score its pages (Quest bound) and store the scores, keeping the
+//   1. score its pages (Quest bound) and store their order keys, keeping the
 //      chunk's physical page numbers in LDS;
 //   2. publish: score_done[list] += 1, then wait until all nc chunks of the
 //      list have published;
@@ -16,7 +16,8 @@
 //      page list at their global ranks);
 //   4. attend to those pages (online softmax) and store one partial record;
 //   5. publish: attn_done[list] += 1; the chunk that completes the count
-//      merges the list's nc partials into out and clears the list's counters.
+//      merges the list's nc partials into out and clears the list's keys,
+//      partials and counters.
 // So only the scores cross between workgroups before the attention, and the
 // page table is read once per page.
 //
@@ -25,11 +26,13 @@
 // its own list, which sit on other workgroups (nc <= grid); every task of the
 // earliest unfinished list is therefore running or about to run after tasks
 // of finished lists, it publishes its scores before it waits, and so the
-// schedule cannot deadlock.  Hand-offs use device-coherent (sc1) data stores,
-// a wait for their completion, then a relaxed counter update.  Every wait is
-// bounded: on timeout ctl.error is set and the kernel still finishes.  The
-// control words live at the head of the caller's workspace: zero before the
-// first call, and every call leaves them zero again.
+// schedule cannot deadlock.  Hand-offs use device-coherent (sc1) data stores
+// of words that are never 0 once written (order keys, sentinel-encoded
+// partials) and a relaxed counter update that does not wait for the stores to
+// land: a reader that has seen the counter re-reads any word still 0.  Every
+// wait is bounded: on timeout ctl.error is set and the kernel still finishes.
+// The control words, keys and partials live in the caller's workspace: zero
+// before the first call, and every call leaves them zero again.
 #include "sa_dev_score.h"
 #include "sa_dev_topk.h"
 #include "sa_step.h"
@@ -59,10 +62,10 @@ __device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t target
   __syncthreads();
 }
 
-// Every thread's hand-off stores have completed; then thread 0 bumps *ctr and
-// gets its old value.
+// Thread 0 bumps *ctr once every thread has issued its hand-off stores, and
+// gets the old value.  The counter does not wait for those stores to land: the
+// handed-off words are 0 until written, and readers re-read the ones not yet there.
 __device__ __forceinline__ uint32_t publish_add(uint32_t* ctr) {
-  stores_done();
   __syncthreads();
   uint32_t old = 0;
   if (threadIdx.x == 0)
@@ -101,7 +104,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     const int c_end = min(c0 + P.chunk_pages, A.max_pages);
     int n = 0;
     for (int p0 = c0; p0 < c_end; p0 += kScorePass)
-      n = quest_score_range<KT, QT, G, kScoreIT, true, kStepWaves>(A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row,
+      n = quest_score_range<KT, QT, G, kScoreIT, true, kStepWaves, true>(A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row,
                                                        p0, min(p0 + kScorePass, c_end), A.lens + b,
                                                        A.max_pages, sc_row, s_pp + (p0 - c0));
     const int L = clamp_len(A.lens[b], A.max_pages);
@@ -114,13 +117,13 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
 
     // 3. the list's selection; keep this chunk's part
     int32_t* sel_row = A.sel ? A.sel + (size_t)i * A.max_sel : nullptr;
-    topk_core<kStepThreads, KPT, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
+    topk_core<kStepThreads, KPT, true, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
                                        [&](int rank, int u) {
                                          if (u >= c0 && u < c1) {
                                            s_kept[u - c0] = 1;
                                            if (sel_row && rank < A.max_sel) sel_row[rank] = u;
                                          }
-                                       }, sel_row != nullptr);
+                                       }, sel_row != nullptr, &A.ctl->error);
     if (sel_row && c == 0) {  // count and padding of the optional page list
       const int cnt = min(min(n, A.n_head + A.k_compete + A.n_tail), A.max_sel);
       for (int j = cnt + tid; j < A.max_sel; j += kStepThreads) sel_row[j] = -1;
@@ -146,7 +149,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
 
     // 4. attention over the chunk's kept pages
     float* part_list = A.partials + (size_t)i * P.nc * G * kPartStride;
-    attend_range<KT, QT, G, 1, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
+    attend_range<KT, QT, G, 1, true, kStepWaves, true>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
                                      pt_row, L, nullptr, 0, s_cnt, A.scale_log2,
                                      part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
     // 5. publish; the list's last chunk merges
@@ -154,9 +157,15 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     if (tid == 0) s_flag = old == (uint32_t)(P.nc - 1);
     __syncthreads();
     if (s_flag) {
-      merge_list<true>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim,
-                       sm.merge);
-      if (tid == 0) {  // every chunk of this list has finished: clear its counters
+      merge_list<true, true, 4>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim,
+                             sm.merge, &A.ctl->error);
+      // every chunk of this list has read the list's keys and partials: return them,
+      // and the counters, to the unwritten state (0) for the next call
+      uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
+      for (int j = tid; j < A.max_pages; j += kStepThreads) st_x<true>(kw + j, 0u);
+      uint32_t* pw = reinterpret_cast<uint32_t*>(part_list);
+      for (int j = tid; j < P.nc * G * kPartStride; j += kStepThreads) st_x<true>(pw + j, 0u);
+      if (tid == 0) {
         st_x<true>(&lc->score_done, 0u);
         st_x<true>(&lc->attn_done, 0u);
       }
