@@ -16,8 +16,8 @@
 namespace sa {
 namespace {
 
-constexpr int kScoreIT = 4;                        // loads per lane
-constexpr int kScorePagesPerWG = 8 * kScoreIT;      // 32 pages per workgroup
+constexpr int kScoreIT = 2;                        // load pairs per lane
+constexpr int kScorePagesPerWG = 16 * kScoreIT;     // 32 pages per workgroup
 
 // grid (ceil(max_pages / 32), Hkv, B), block 256
 template <int KT, int QT, int G>

@@ -42,9 +42,9 @@ namespace {
 
 constexpr int kStepWaves = 12;              // one workgroup per CU: 12 waves, 168 VGPRs each
 constexpr int kStepThreads = 64 * kStepWaves;
-constexpr int kScoreIT = (128 + kStepWaves - 1) / kStepWaves;  // loads per lane per score pass
-constexpr int kScorePass = 2 * kStepWaves * kScoreIT;           // pages per score pass (>= 256)
-constexpr int kStepChunkCap = kStepMaxChunk / kScorePass * kScorePass;
+constexpr int kScoreIT = (64 + kStepWaves - 1) / kStepWaves;  // load pairs per lane per score pass
+constexpr int kScorePass = 4 * kStepWaves * kScoreIT;          // pages per score pass (>= 256)
+constexpr int kChunkGrain = 64;                                // chunk sizes are multiples of this
 constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling (each poll is a memory round trip)
 
 // Thread 0 waits until *p >= target; the workgroup then continues.
@@ -205,11 +205,11 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
   P.lists = B * Hkv;
   const long lists = P.lists;
   const long wgs = num_cus;  // resident workgroups aimed for: one per CU
-  // chunks: about one per resident workgroup overall, whole score passes
+  // chunks: about one per resident workgroup overall, in multiples of kChunkGrain pages
   long chunk = (lists * max_pages + wgs - 1) / wgs;
-  chunk = (chunk + kScorePass - 1) / kScorePass * kScorePass;
-  if (chunk < kScorePass) chunk = kScorePass;
-  if (chunk > kStepChunkCap) chunk = kStepChunkCap;
+  chunk = (chunk + kChunkGrain - 1) / kChunkGrain * kChunkGrain;
+  if (chunk < kChunkGrain) chunk = kChunkGrain;
+  if (chunk > kStepMaxChunk) chunk = kStepMaxChunk;
   P.chunk_pages = (int)chunk;
   P.nc = (int)((max_pages + chunk - 1) / chunk);
   P.n_tasks = (int)(lists * P.nc);
