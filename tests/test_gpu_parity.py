@@ -33,6 +33,9 @@ CASES = {
                         mode="sals", k_compete=5),
     "sals_i8_h16": dict(B=1, Hq=16, Hkv=16, lens=(2100,), kv_dtype="i8", q_dtype="bf16",
                         mode="sals", k_compete=4),
+    # many lists x pages, B = 2, ragged: several chunks per list and empty chunks
+    "mha_bf16_b2_long": dict(B=2, Hq=16, Hkv=16, lens=(16384, 9000), kv_dtype="bf16",
+                               q_dtype="bf16", budget_pages=40, page_table="random"),
 }
 
 
