@@ -222,7 +222,7 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  * receive the selection as sa_topk_pages writes it.
  * Quest mode with one query head per kv-head runs as a single persistent
  * kernel whose workgroups hand work to each other through the workspace
- * (control words, score keys, partial records, where 0 means "not written
+ * (an error word, score keys and partial records, where 0 means "not written
  * yet"): the workspace must be zero-filled before its first use, every call
  * leaves those words zero again, and one workspace serves one call at a time.
  * A bounded wait that times out (never expected) sets the 32-bit word at byte

@@ -152,7 +152,7 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   const size_t fused_part = (size_t)L.splan.lists * L.splan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2);
   size_t off = 0;
   L.ctl = off;
-  off = align_up(off + step_ctl_bytes((int)lists));
+  off = align_up(off + step_ctl_bytes());
   L.scores = off;
   off = align_up(off + (L.dense ? 0 : lists * L.max_units * sizeof(float)));
   L.sel = off;
@@ -359,7 +359,6 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
     A.partials = partials;
     A.out = out;
     A.ctl = reinterpret_cast<StepCtl*>(ws + lay.ctl);
-    A.lctl = reinterpret_cast<ListCtl*>(ws + lay.ctl + sizeof(StepCtl));
     StepPlan P = lay.splan;
     P.grid = P.n_tasks < wgs ? P.n_tasks : wgs;
     return hip_status(launch_quest_step(kv->dtype, q_dtype, A, P, st));

@@ -12,18 +12,12 @@ constexpr int kStepMaxPages = 4096;          // top-K keys of a list stay in reg
 constexpr int kStepMaxPhysPages = 1 << 27;   // resolved pages pack the page id in 27 bits
 constexpr int kStepMaxChunk = 1024;          // pages per chunk task (kept in LDS)
 
-// Control words at the head of the step workspace.
+// Control word record at the head of the step workspace.
 struct StepCtl {
   uint32_t reserved[2];
   uint32_t error;  // nonzero after a bounded wait timed out
   uint32_t pad[13];
 };
-struct ListCtl {  // one 64-byte record per (batch, kv-head) list
-  uint32_t score_done;  // chunks whose scores are stored
-  uint32_t attn_done;   // chunks whose partial record is stored
-  uint32_t pad[14];
-};
-
 struct StepPlan {
   int lists;        // B * Hkv
   int chunk_pages;  // pages per chunk task (multiple of 64, <= kStepMaxChunk)
@@ -49,7 +43,6 @@ struct StepArgs {
   float* partials;  // [lists][nc][G][kHeadDim + 2]
   float* out;       // [B][hq][kHeadDim]
   StepCtl* ctl;
-  ListCtl* lctl;
 };
 
 StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_cus);
@@ -57,7 +50,7 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
 int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus);
 // Top-K keys per thread of the fused kernel for lists of up to max_pages pages.
 int step_kpt(int max_pages);
-size_t step_ctl_bytes(int lists);
+size_t step_ctl_bytes();
 hipError_t launch_quest_step(int kv_dtype, int q_dtype, const StepArgs& A, const StepPlan& P,
                              hipStream_t st);
 

@@ -8,31 +8,31 @@
 // pages; one task per chunk does, in one workgroup:
 //   1. score its pages (Quest bound) and store their order keys, keeping the
 //      chunk's physical page numbers in LDS;
-//   2. publish: score_done[list] += 1, then wait until all nc chunks of the
-//      list have published;
-//   3. run the exact top-K of the whole list from all of its scores -- every
+//   2. run the exact top-K of the whole list from all of its keys -- every
 //      chunk of the list computes the same selection -- and keep only the
 //      selected pages of its own chunk (writing their entries of the optional
 //      page list at their global ranks);
-//   4. attend to those pages (online softmax) and store one partial record;
-//   5. publish: attn_done[list] += 1; the chunk that completes the count
-//      merges the list's nc partials into out and clears the list's keys,
-//      partials and counters.
+//   3. attend to those pages (online softmax) and store one partial record;
+//   4. chunk 0 merges the list's nc partial records into out and clears the
+//      list's keys and partials.
 // So only the scores cross between workgroups before the attention, and the
 // page table is read once per page.
 //
+// Hand-offs need no counters: every handed-off word is nonzero once written
+// (order keys; partial words XOR a constant that no fp32 result takes), the
+// workspace holds zeros before the call, and a reader re-reads, device-
+// coherently, every word still 0 until all have arrived.  Stores are relaxed
+// and device-coherent (sc1) and nobody waits for them to land.  Every re-read
+// loop is bounded: on timeout ctl.error is set and the kernel still finishes.
+// The keys and partials of a list are returned to 0 by its merger, which runs
+// only after every chunk of the list has stored its partial record and so has
+// finished reading keys.
+//
 // Scheduling: task t runs on workgroup t mod grid, in order; every workgroup
 // is co-resident and grid >= nc.  A task waits only for the other chunks of
-// its own list, which sit on other workgroups (nc <= grid); every task of the
-// earliest unfinished list is therefore running or about to run after tasks
-// of finished lists, it publishes its scores before it waits, and so the
-// schedule cannot deadlock.  Hand-offs use device-coherent (sc1) data stores
-// of words that are never 0 once written (order keys, sentinel-encoded
-// partials) and a relaxed counter update that does not wait for the stores to
-// land: a reader that has seen the counter re-reads any word still 0.  Every
-// wait is bounded: on timeout ctl.error is set and the kernel still finishes.
-// The control words, keys and partials live in the caller's workspace: zero
-// before the first call, and every call leaves them zero again.
+// its own list, which sit on other workgroups (nc <= grid) behind tasks of
+// earlier lists only; the earliest unfinished list therefore always makes
+// progress, and the schedule cannot deadlock.
 #include "sa_dev_score.h"
 #include "sa_dev_topk.h"
 #include "sa_step.h"
@@ -45,33 +45,6 @@ constexpr int kStepThreads = 64 * kStepWaves;
 constexpr int kScoreIT = (64 + kStepWaves - 1) / kStepWaves;  // load pairs per lane per score pass
 constexpr int kScorePass = 4 * kStepWaves * kScoreIT;          // pages per score pass (>= 256)
 constexpr int kChunkGrain = 64;                                // chunk sizes are multiples of this
-constexpr uint32_t kSpinLimit = 1u << 18;  // ~0.3 s of polling (each poll is a memory round trip)
-
-// Thread 0 waits until *p >= target; the workgroup then continues.
-__device__ __forceinline__ void wait_at_least(const uint32_t* p, uint32_t target, uint32_t* err) {
-  if (threadIdx.x == 0) {
-    uint32_t spins = 0;
-    while (ld_x<true>(p) < target) {
-      __builtin_amdgcn_s_sleep(1);
-      if (++spins > kSpinLimit) {
-        __hip_atomic_fetch_or(err, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-    }
-  }
-  __syncthreads();
-}
-
-// Thread 0 bumps *ctr once every thread has issued its hand-off stores, and
-// gets the old value.  The counter does not wait for those stores to land: the
-// handed-off words are 0 until written, and readers re-read the ones not yet there.
-__device__ __forceinline__ uint32_t publish_add(uint32_t* ctr) {
-  __syncthreads();
-  uint32_t old = 0;
-  if (threadIdx.x == 0)
-    old = __hip_atomic_fetch_add(ctr, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-  return old;
-}
 
 template <int G>
 union StepSmem {
@@ -87,14 +60,13 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
   __shared__ int32_t s_pp[kStepMaxChunk];    // physical page of each chunk page, or -1
   __shared__ int32_t s_kept[kStepMaxChunk];  // chunk page kept by the selection
   __shared__ int32_t s_list[kStepMaxChunk];  // kept pages: (physical << 4) | (valid - 1)
-  __shared__ int s_cnt, s_flag;
+  __shared__ int s_cnt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = A.hkv * G;
 
   for (int t = blockIdx.x; t < P.n_tasks; t += gridDim.x) {
     const int i = t / P.nc, c = t % P.nc;
     const int b = i / A.hkv, h = i % A.hkv;
-    ListCtl* lc = A.lctl + i;
     const int32_t* pt_row = A.pt + (size_t)b * A.max_pages;
     const int c0 = c * P.chunk_pages;
     float* sc_row = A.scores + (size_t)i * A.max_pages;
@@ -111,11 +83,9 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     if (c0 >= c_end) n = (L + kPage - 1) / kPage;
     const int c1 = min(c0 + P.chunk_pages, n);  // c1 <= c0: an empty chunk
     for (int j = tid; j < P.chunk_pages; j += kStepThreads) s_kept[j] = 0;
-    // 2. publish, then wait for the list's other chunks
-    publish_add(&lc->score_done);
-    wait_at_least(&lc->score_done, (uint32_t)P.nc, &A.ctl->error);
+    __syncthreads();  // the clears (and s_pp) before the selection marks kept pages
 
-    // 3. the list's selection; keep this chunk's part
+    // 2. the list's selection (its keys re-read until all have arrived); keep this chunk's part
     int32_t* sel_row = A.sel ? A.sel + (size_t)i * A.max_sel : nullptr;
     topk_core<kStepThreads, KPT, true, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
                                        [&](int rank, int u) {
@@ -147,30 +117,24 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     }
     __syncthreads();
 
-    // 4. attention over the chunk's kept pages
+    // 3. attention over the chunk's kept pages
     float* part_list = A.partials + (size_t)i * P.nc * G * kPartStride;
     attend_range<KT, QT, G, 1, true, kStepWaves, true>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
                                      pt_row, L, nullptr, 0, s_cnt, A.scale_log2,
                                      part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
-    // 5. publish; the list's last chunk merges
-    const uint32_t old = publish_add(&lc->attn_done);
-    if (tid == 0) s_flag = old == (uint32_t)(P.nc - 1);
-    __syncthreads();
-    if (s_flag) {
+    // 4. chunk 0 merges the list's partial records as they arrive
+    if (c == 0) {
+      __syncthreads();  // the attention's shared memory is free before the merge reuses it
       merge_list<true, true, 4>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim,
                              sm.merge, &A.ctl->error);
-      // every chunk of this list has read the list's keys and partials: return them,
-      // and the counters, to the unwritten state (0) for the next call
+      // every chunk of this list has read the list's keys (before storing its
+      // partial record): return keys and partials to the unwritten state (0)
       uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
       for (int j = tid; j < A.max_pages; j += kStepThreads) st_x<true>(kw + j, 0u);
       uint32_t* pw = reinterpret_cast<uint32_t*>(part_list);
       for (int j = tid; j < P.nc * G * kPartStride; j += kStepThreads) st_x<true>(pw + j, 0u);
-      if (tid == 0) {
-        st_x<true>(&lc->score_done, 0u);
-        st_x<true>(&lc->attn_done, 0u);
-      }
     }
-    __syncthreads();  // shared memory and s_flag are reused by the next task
+    __syncthreads();  // shared memory is reused by the next task
   }
 }
 
@@ -217,7 +181,7 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
   return P;
 }
 
-size_t step_ctl_bytes(int lists) { return sizeof(StepCtl) + (size_t)lists * sizeof(ListCtl); }
+size_t step_ctl_bytes() { return sizeof(StepCtl); }
 
 int step_kpt(int max_pages) { return max_pages <= kStepThreads * kKptLo ? kKptLo : kKptHi; }
 
