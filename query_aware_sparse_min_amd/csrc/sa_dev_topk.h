@@ -18,7 +18,8 @@
 // so that all waves agree on the digit without a second barrier.  Three
 // histograms rotate, each cleared two passes before its next use.  The passes
 // stop once the threshold prefix is fully determined or once every key that
-// carries it is kept.  One block scan of (#keys above, #keys at the threshold)
+// carries it is kept (a few keys left at the threshold cost one more cheap
+// pass, which beats ranking them).  One block scan of (#keys above, #keys at the threshold)
 // then ranks every kept unit in index order: a unit at the threshold is kept
 // iff fewer than r such units precede it (the lower-index tie rule), and its
 // rank is its output slot, so the list comes out ascending without sorting.
@@ -36,18 +37,11 @@ namespace sa {
 constexpr int kTopkDigit = 8;
 constexpr int kTopkBins = 1 << kTopkDigit;
 
-constexpr int kTopkCand = 64;  // threshold bins this small are resolved by one wave
-
 template <int NT>
 struct TopkSmem {
   alignas(16) uint32_t hist[3][kTopkBins];
   uint32_t wmin[NT / 64], wmax[NT / 64];
   uint32_t wa[NT / 64], wb[NT / 64];
-  // keys of the threshold bin: (key << 32) | ~unit, so that a larger value is
-  // the better unit under (key desc, unit asc)
-  unsigned long long cand[kTopkCand];
-  uint32_t crank[kTopkCand];  // number of better candidates
-  int ncand;
   int last_kept;
 };
 
@@ -128,13 +122,10 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   };
 
   for (int i = tid; i < 3 * kTopkBins; i += NT) (&sm.hist[0][0])[i] = 0u;
-  for (int i = tid; i < kTopkCand; i += NT) sm.crank[i] = 0u;
-  if (tid == 0) sm.ncand = 0;
 
   // threshold: keys whose bits under mask dm equal tval ("at" keys, cbin of
   // them); rem of them are kept, every key above is kept
   uint32_t dm = 0xFFFFFFFFu, tval = 0xFFFFFFFFu, rem = 0, cbin = 0;
-  bool cand = false;  // the at keys are few: one wave ranks them exactly
   if (k > 0) {
     uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
     for_keys([&](int, uint32_t x) { kmin = min(kmin, x); kmax = max(kmax, x); });
@@ -168,6 +159,7 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
         }
         // every wave: lane l holds bins 255-4l .. 252-4l, largest first
         const uint4 hv = *reinterpret_cast<const uint4*>(&H[kTopkBins - 4 - 4 * lane]);
+        const uint32_t c4[4] = {hv.w, hv.z, hv.y, hv.x};
         const uint32_t tot = hv.x + hv.y + hv.z + hv.w;
         const uint32_t incl = wave_incl_scan_u32(tot);
         uint32_t before = incl - tot;
@@ -176,7 +168,6 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
         int bin = 0;
         uint32_t nrem = 0;
         cbin = 0;
-        const uint32_t c4[4] = {hv.w, hv.z, hv.y, hv.x};
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) {
           if (before < rem && rem <= before + c4[jj]) {
@@ -193,56 +184,13 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
         dm |= dmask << shift;
         nb = shift;
         if (nb == 0 || cbin == rem) break;  // fully determined, or the whole bin is kept
-        if (cbin <= (uint32_t)kTopkCand) {
-          cand = true;
-          break;
-        }
       }
     }
-    if (!cand && cbin != rem && cbin <= (uint32_t)kTopkCand) cand = true;  // exact ties, few
   }
-  int cslot[KPT > 0 ? KPT : 1];  // candidate slot of each register key
-  if (cand) {
-    // gather the at keys and rank them by (key desc, unit asc): lane i of wave w
-    // counts the candidates of the w-th slice that beat candidate i
-    for_keys([&](int j, uint32_t x) {
-      if ((x & dm) == tval) {
-        const int slot = atomicAdd(&sm.ncand, 1);
-        sm.cand[slot] = ((unsigned long long)x << 32) | (uint32_t)~(uint32_t)(n_head + r0 + j);
-        if constexpr (KPT > 0) cslot[j] = slot;
-      }
-    });
-    __syncthreads();
-    {
-      const int nc = __builtin_amdgcn_readfirstlane((int)cbin);
-      const int per = (nc + NW - 1) / NW;
-      const int j0 = wave * per, j1 = min(nc, j0 + per);
-      if (lane < nc && j0 < j1) {
-        const unsigned long long me = sm.cand[lane];
-        uint32_t rk = 0;
-        for (int j = j0; j < j1; ++j) rk += sm.cand[j] > me ? 1u : 0u;
-        if (rk) atomicAdd(&sm.crank[lane], rk);
-      }
-    }
-    __syncthreads();
-  }
-  // is the at key j of this thread kept?  (only asked when cand)
-  auto cand_kept = [&](int j) -> bool {
-    if constexpr (KPT > 0) {
-      return sm.crank[cslot[j]] < rem;
-    } else {  // keys re-read: find the unit among the candidates
-      const int u = n_head + r0 + j, nc = (int)cbin;
-      bool r = false;
-      for (int s2 = 0; s2 < nc; ++s2)
-        if ((uint32_t)~(uint32_t)sm.cand[s2] == (uint32_t)u) r = sm.crank[s2] < rem;
-      return r;
-    }
-  };
-
-  // At keys are kept by the candidate ranks (cand), all of them (cbin == rem),
-  // or else the first rem in unit order, which needs a block scan of the at
-  // keys; the output ranks need a block scan of the kept keys.
-  const bool tie_scan = k > 0 && !cand && cbin != rem;
+  // At keys are all kept (cbin == rem), or else (exact ties) the first rem in
+  // unit order, which needs a block scan of the at keys; the output ranks
+  // need a block scan of the kept keys.
+  const bool tie_scan = k > 0 && cbin != rem;
   const bool scan = k > 0 && (tie_scan || want_rank);
   uint32_t kept_before = 0, eq_seen = 0;
   if (scan) {
@@ -250,7 +198,7 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
     for_keys([&](int j, uint32_t x) {
       const uint32_t xm = x & dm;
       gt += xm > tval;
-      if (xm == tval) eq += (!cand || cand_kept(j)) ? 1u : 0u;
+      eq += xm == tval;
     });
     const uint32_t ga = wave_incl_scan_u32(gt), ea = wave_incl_scan_u32(eq);
     if (lane == 63) { sm.wa[wave] = ga; sm.wb[wave] = ea; }
@@ -268,9 +216,7 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
       const uint32_t xm = x & dm;
       bool kp = xm > tval;
       if (xm == tval) {
-        if (cand) {
-          kp = cand_kept(j);
-        } else if (tie_scan) {
+        if (tie_scan) {
           kp = eq_seen < rem;
           ++eq_seen;
         } else {

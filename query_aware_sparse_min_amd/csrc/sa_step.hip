@@ -58,7 +58,8 @@ template <int KT, int QT, int G, int KPT>
 __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A, StepPlan P) {
   __shared__ StepSmem<G> sm;
   __shared__ int32_t s_pp[kStepMaxChunk];    // physical page of each chunk page, or -1
-  __shared__ int32_t s_kept[kStepMaxChunk];  // chunk page kept by the selection
+  // chunk page kept by the selection: (physical << 4) | (valid - 1), else -1
+  __shared__ int32_t s_kept[kStepMaxChunk];
   __shared__ int32_t s_list[kStepMaxChunk];  // kept pages: (physical << 4) | (valid - 1)
   __shared__ int s_cnt;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -82,7 +83,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     const int L = clamp_len(A.lens[b], A.max_pages);
     if (c0 >= c_end) n = (L + kPage - 1) / kPage;
     const int c1 = min(c0 + P.chunk_pages, n);  // c1 <= c0: an empty chunk
-    for (int j = tid; j < P.chunk_pages; j += kStepThreads) s_kept[j] = 0;
+    for (int j = tid; j < P.chunk_pages; j += kStepThreads) s_kept[j] = -1;
     __syncthreads();  // the clears (and s_pp) before the selection marks kept pages
 
     // 2. the list's selection (its keys re-read until all have arrived); keep this chunk's part
@@ -90,7 +91,8 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     topk_core<kStepThreads, KPT, true, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
                                        [&](int rank, int u) {
                                          if (u >= c0 && u < c1) {
-                                           s_kept[u - c0] = 1;
+                                           const int pp = s_pp[u - c0];
+                                           if (pp >= 0) s_kept[u - c0] = (pp << 4) | (min(kPage, L - u * kPage) - 1);
                                            if (sel_row && rank < A.max_sel) sel_row[rank] = u;
                                          }
                                        }, sel_row != nullptr, &A.ctl->error);
@@ -100,18 +102,23 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
       if (tid == 0) A.num_sel[i] = cnt;
     }
     __syncthreads();
-    if (wave == 0) {  // kept pages of the chunk, ascending, resolved through the page table
+    if (wave == 0) {  // kept pages of the chunk, ascending (four reads in flight per round)
+      const int nch = c1 - c0;
       int cnt = 0;
-      for (int base = 0; base < c1 - c0; base += 64) {
-        const int j = base + lane;
-        const int pp = j < c1 - c0 ? s_pp[j] : -1;
-        const bool kf = j < c1 - c0 && s_kept[j] != 0 && pp >= 0;
-        const uint64_t bal = __ballot(kf);
-        if (kf) {
-          const int pos = cnt + __popcll(bal & ((1ull << lane) - 1ull));
-          s_list[pos] = (pp << 4) | (min(kPage, L - (c0 + j) * kPage) - 1);
+      for (int base = 0; base < nch; base += 256) {
+        int32_t v[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int j = base + 64 * q + lane;
+          const int32_t x = s_kept[min(j, kStepMaxChunk - 1)];
+          v[q] = j < nch ? x : -1;
         }
-        cnt += __popcll(bal);
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const uint64_t bal = __ballot(v[q] >= 0);
+          if (v[q] >= 0) s_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = v[q];
+          cnt += __popcll(bal);
+        }
       }
       if (lane == 0) s_cnt = cnt;
     }
