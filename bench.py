@@ -56,6 +56,9 @@ def parse():
     ap.add_argument("--cpu-seconds", type=float, default=12.0)
     ap.add_argument("--pmc-run", action="store_true",
                     help="run a few steps and a plain copy of known size, for a counter run")
+    ap.add_argument("--configs", default="",
+                    help="instead of the headline line, one line per listed workload "
+                         "(1-5, 5d = config 5 with every page kept), e.g. --configs 1,3,4,5,5d")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc outputs")
     return ap.parse_args()
@@ -117,6 +120,10 @@ def main():
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
               f"(this path has no multi-GPU part)", file=sys.stderr)
         sys.exit(2)
+    if args.configs:
+        for name in args.configs.split(","):
+            config_line(name.strip(), args)
+        return
     import numpy as np
     import torch
 
@@ -296,6 +303,112 @@ def main():
         "setup_s": round(setup_s, 1),
     }
     print(json.dumps(rec), flush=True)
+
+
+CONFIG_COPIES_BYTES = 4 << 30  # layer copies rotated: at least this many bytes of K/V in all
+
+
+def config_line(name, args):
+    """One workload at full size on one GPU: the decode step (graph of K steps over
+    rotated layer copies, fresh query each), its algorithmic bytes and GB/s, and
+    dense flash-decode over every page of the same copies for comparison."""
+    import numpy as np
+    import torch
+
+    import query_aware_sparse_min_amd as sa
+    import synth
+
+    if not os.path.exists(sa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    sa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    t0 = time.time()
+    print(f"[bench] config {name}: generating inputs", file=sys.stderr, flush=True)
+    wl = synth.make_config(int(name[0]), dense=name.endswith("d"))
+    d = synth.to_device(wl, dev)
+    print(f"[bench] config {name}: inputs on the GPU after {time.time() - t0:.0f} s", file=sys.stderr,
+          flush=True)
+    seqs = sa.Seqs(d.page_table, d.seq_lens)
+    mode = sa.SA_MODE_QUEST if wl.mode == "quest" else sa.SA_MODE_SALS
+    cfg = sa.SelectCfg(mode, wl.unit_tokens, wl.k_compete, wl.n_head_forced, wl.n_tail_forced,
+                       wl.rank, d.proj, wl.lse_scale)
+    kv_bytes = d.k.numel() * d.k.element_size() * 2
+    R = int(max(2, min(args.copies, -(-CONFIG_COPIES_BYTES // kv_bytes))))
+    copies = []
+    for r in range(R):
+        k = d.k if r == 0 else d.k.clone()
+        v = d.v if r == 0 else d.v.clone()
+        kv = sa.KVCache(k, v, d.k_scale, d.v_scale)
+        meta, mscale = sa.alloc_meta(kv, cfg)
+        sa.sa_build_page_meta(kv, seqs, cfg, meta, mscale)
+        copies.append((kv, meta, mscale))
+    NQ = 16
+    qs = [synth.q_to_device(wl, synth.fresh_q(wl, i), dev) for i in range(NQ)]
+    ws = sa.alloc_workspace(sa.sa_decode_step_workspace_size(wl.Hq, copies[0][0], seqs, cfg), dev)
+    out = torch.empty((wl.B, wl.Hq, wl.d), dtype=torch.float32, device=dev)
+    ms = sa.sa_max_selected(seqs, cfg)
+    setup_s = time.time() - t0
+    stream = torch.cuda.current_stream()
+
+    def step(i):
+        kv, meta, mscale = copies[i % R]
+        sa.sa_decode_step(qs[i % NQ], kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws)
+
+    def graph_us(fn, n):
+        for i in range(min(n, args.warmup)):
+            fn(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        cap = torch.cuda.Stream()
+        cap.wait_stream(stream)
+        with torch.cuda.stream(cap):
+            with torch.cuda.graph(g, stream=cap):
+                for i in range(n):
+                    fn(args.warmup + i)
+        stream.wait_stream(cap)
+        g.replay()
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        g.replay()
+        b.record(stream)
+        torch.cuda.synchronize()
+        return a.elapsed_time(b) / n * 1e3
+
+    K = max(10, min(args.steps, 100))
+    step_us = graph_us(step, K)
+    num = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)
+    sel = torch.empty((wl.B, wl.Hkv, ms), dtype=torch.int32, device=dev)
+    kv, meta, mscale = copies[0]
+    sa.sa_decode_step(qs[0], kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws, sel, num)
+    torch.cuda.synchronize()
+    nb = synth.step_bytes(wl, num.cpu().numpy())
+    dws = sa.alloc_workspace(sa.sa_attn_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.max_pages, 0), dev)
+    dense_us = graph_us(lambda i: sa.sa_sparse_decode_attn(qs[i % NQ], copies[i % R][0], seqs, None,
+                                                           None, wl.softmax_scale, out, dws),
+                        max(10, K // 4))
+    gbs = nb["total"] / (step_us * 1e-6) / 1e9
+    dense_b = synth.dense_bytes(wl)
+    rec = {
+        "metric": f"decode-step µs + effective HBM GB/s, {wl.name}",
+        "workload": wl.name, "batch": wl.B, "num_q_heads": wl.Hq, "num_kv_heads": wl.Hkv,
+        "context": [int(x) for x in np.unique(wl.seq_lens)][:4], "kv_dtype": wl.kv_dtype,
+        "scoring": "quest min/max bound" if wl.mode == "quest" else "sals int4 index + block lse",
+        "kept_units": int(wl.n_head_forced + wl.k_compete + wl.n_tail_forced),
+        "step_us": round(step_us, 2), "step_bytes": nb["total"],
+        "bytes": {k2: int(v2) for k2, v2 in nb.items()},
+        "gbs": round(gbs, 1), "hbm_peak_frac": round(gbs / PEAK_GBS, 4),
+        "dense_us": round(dense_us, 2),
+        "dense_gbs": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
+        "speedup_vs_dense": round(dense_us / step_us, 2),
+        "layer_copies_rotated": R, "steps": K, "setup_s": round(setup_s, 1),
+        "timing": "HIP graph of K steps, replayed once between two events",
+    }
+    print(json.dumps(rec), flush=True)
+    del copies, d, ws, dws
+    torch.cuda.empty_cache()
 
 
 def cpu_baseline(wl, seconds, step_bytes):

@@ -1,28 +1,28 @@
-// sa_topk.hip - standalone exact top-K (sa_topk_pages): one 256-thread
-// workgroup per (batch, kv-head) list running topk_list of sa_dev_topk.h.
+// sa_topk.hip - standalone exact top-K (sa_topk_pages): one workgroup per
+// (batch, kv-head) list running topk_list of sa_dev_topk.h; 256 threads for
+// lists of up to 4096 units, 1024 threads for longer ones.
 #include "sa_dev_topk.h"
 
 namespace sa {
 namespace {
 
-constexpr int kTopkThreads = 256;
-constexpr int kTopkKPT = 16;  // register-resident keys per thread: lists of up to 4096 units
+constexpr int kTopkKPT = 16;  // register-resident keys per thread
 
-// grid (Hkv, B), block 256.  KPT = 0: keys re-read from the scores (long lists).
-template <int KPT>
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(
+// grid (Hkv, B), block NT.  KPT = 0: keys re-read from the scores (lists
+// longer than NT * 16 units).
+template <int NT, int KPT>
+__global__ __launch_bounds__(NT) void topk_kernel(
     const float* __restrict__ scores, int max_units, int hkv, const int32_t* __restrict__ lens,
     int max_pages, int unit_tokens, int k, int n_head, int n_tail, int32_t* __restrict__ sel,
     int32_t* __restrict__ num_sel, int max_sel) {
-  __shared__ TopkSmem<kTopkThreads> sm;
+  __shared__ TopkSmem<NT> sm;
   const int h = blockIdx.x, b = blockIdx.y;
   const int L = clamp_len(lens[b], max_pages);
   const int n = (L + unit_tokens - 1) / unit_tokens;
   const int np = (L + kPage - 1) / kPage;
   const size_t list = (size_t)b * hkv + h;
-  topk_list<kTopkThreads, KPT, false>(scores ? scores + list * max_units : nullptr, n, np,
-                                      unit_tokens / kPage, k, n_head, n_tail,
-                                      sel + list * max_sel, num_sel + list, max_sel, sm);
+  topk_list<NT, KPT, false>(scores ? scores + list * max_units : nullptr, n, np, unit_tokens / kPage,
+                            k, n_head, n_tail, sel + list * max_sel, num_sel + list, max_sel, sm);
 }
 
 }  // namespace
@@ -30,12 +30,16 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(
 hipError_t launch_topk(const float* scores, int max_units, const Shapes& s, const int32_t* lens,
                        int unit_tokens, int k, int n_head, int n_tail, int32_t* sel,
                        int32_t* num_sel, int max_sel, hipStream_t st) {
-  if (max_units <= kTopkThreads * kTopkKPT)
-    hipLaunchKernelGGL(topk_kernel<kTopkKPT>, dim3(s.Hkv, s.B), dim3(kTopkThreads), 0, st, scores,
+  if (max_units <= 256 * kTopkKPT)
+    hipLaunchKernelGGL((topk_kernel<256, kTopkKPT>), dim3(s.Hkv, s.B), dim3(256), 0, st, scores,
+                       max_units, s.Hkv, lens, s.max_pages, unit_tokens, k, n_head, n_tail, sel,
+                       num_sel, max_sel);
+  else if (max_units <= 1024 * kTopkKPT)
+    hipLaunchKernelGGL((topk_kernel<1024, kTopkKPT>), dim3(s.Hkv, s.B), dim3(1024), 0, st, scores,
                        max_units, s.Hkv, lens, s.max_pages, unit_tokens, k, n_head, n_tail, sel,
                        num_sel, max_sel);
   else
-    hipLaunchKernelGGL(topk_kernel<0>, dim3(s.Hkv, s.B), dim3(kTopkThreads), 0, st, scores,
+    hipLaunchKernelGGL((topk_kernel<1024, 0>), dim3(s.Hkv, s.B), dim3(1024), 0, st, scores,
                        max_units, s.Hkv, lens, s.max_pages, unit_tokens, k, n_head, n_tail, sel,
                        num_sel, max_sel);
   return hipGetLastError();

@@ -36,6 +36,9 @@ CASES = {
     # many lists x pages, B = 2, ragged: several chunks per list and empty chunks
     "mha_bf16_b2_long": dict(B=2, Hq=16, Hkv=16, lens=(16384, 9000), kv_dtype="bf16",
                                q_dtype="bf16", budget_pages=40, page_table="random"),
+    # a list of 18750 pages: the top-K that re-reads its keys from the scores
+    "gqa2_bf16_18k_pages": dict(B=1, Hq=2, Hkv=1, lens=(300000,), kv_dtype="bf16",
+                                q_dtype="bf16", budget_pages=64),
 }
 
 
