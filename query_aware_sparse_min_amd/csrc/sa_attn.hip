@@ -28,8 +28,13 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   }
   const int j0 = split * pps, j1 = min(j0 + pps, cnt);
   float* part = partials + (((size_t)b * hkv + h) * nsplit + split) * G * kPartStride;
-  attend_range<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
-                          lst, j0, j1, scale_log2, part, sm);
+  // four or more bf16 query heads per kv-head: scores on the matrix cores
+  if constexpr (G >= 4 && QT == SA_BF16 && (KT == SA_BF16 || KT == SA_I8))
+    attend_range_mfma<KT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
+                             lst, j0, j1, scale_log2, part, sm);
+  else
+    attend_range<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
+                            lst, j0, j1, scale_log2, part, sm);
 }
 
 // grid (Hkv, B), block 256: merge the splits of one list

@@ -17,6 +17,8 @@
 // {acc[128], max, sum} per query head.
 #pragma once
 
+#include <type_traits>
+
 #include "sa_internal.h"
 
 namespace sa {
@@ -75,63 +77,47 @@ struct PageRef {
   int nv;  // valid tokens
 };
 
-// Attend to pages lst[j0 .. j1) (lst == nullptr: logical pages j0 .. j1) of
-// list (b, h) and write the workgroup's partial records to part[G][kPartStride].
-// rlst (optional; LDS or memory written before the launch) holds the pages
-// already resolved to (physical page << 4) | (valid tokens - 1), read with
-// plain loads; the page table is then not read.
-// PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
-// COH: lst is read and the partials are written device-coherently; ENC: the
-// partial words are stored as (bits ^ kPartSentinel).
-template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4, bool ENC = false>
-__device__ __forceinline__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
-                             const void* __restrict__ v, const uint16_t* __restrict__ ks,
-                             const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
-                             const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
-                             int j1, float scale_log2, float* __restrict__ part,
-                             AttnSmem<G, NW>& sm, const int32_t* rlst = nullptr) {
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int r = lane >> 4, c = lane & 15;
-  const int hq = hkv * G;
-  const int np = (L + kPage - 1) / kPage;
-
-  float qv[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) load8<QT>(q, ((size_t)b * hq + (size_t)h * G + g) * kHeadDim + 8 * c, qv[g]);
-
-  float m[G], l[G], acc[G][8];
-#pragma unroll
-  for (int g = 0; g < G; ++g) {
-    m[g] = -INFINITY;
-    l[g] = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
-  }
-
-  // Resolve this wave's pages j = j0 + wave + NW * x (x < 64) up front: lane x
-  // loads list entry x, then its page-table entry, so the list and the page
-  // table cost one memory round trip each instead of one per page.
+// The pages j = j0 + wave, j0 + wave + NW, ... (< j1) that one wave takes from
+// a list: lst[j] (lst == nullptr: logical page j) through the page table, or
+// rlst[j] already resolved to (physical page << 4) | (valid tokens - 1).  The
+// first 64 are resolved up front, lane x holding the x-th, so the list and the
+// page table cost one memory round trip each instead of one per page.
+template <bool COH, int NW>
+struct WavePages {
+  const int32_t* pt_row;
+  const int32_t* lst;
+  const int32_t* rlst;
+  int j0, j1, np, num_pages, L, wave;
   int my_pp = -1, my_nv = 0;
-  if (rlst) {
+
+  __device__ __forceinline__ WavePages(const int32_t* pt_row_, const int32_t* lst_,
+                                       const int32_t* rlst_, int j0_, int j1_, int L_,
+                                       int num_pages_)
+      : pt_row(pt_row_), lst(lst_), rlst(rlst_), j0(j0_), j1(j1_),
+        np((L_ + kPage - 1) / kPage), num_pages(num_pages_), L(L_),
+        wave((int)(threadIdx.x >> 6)) {
+    const int lane = threadIdx.x & 63;
     const int j = j0 + wave + NW * lane;
-    const int32_t r = j < j1 ? rlst[j] : -1;
-    if (r >= 0) {
-      my_pp = r >> 4;
-      my_nv = (r & 15) + 1;
-    }
-  } else {
-    const int j = j0 + wave + NW * lane;
-    int p = -1;
-    if (j < j1) p = lst ? ld_x<COH>(lst + j) : j;
-    if (p >= 0 && p < np) {
-      const int pp = pt_row[p];
-      if (pp >= 0 && pp < num_pages) {
-        my_pp = pp;
-        my_nv = min(kPage, L - p * kPage);
+    if (rlst) {
+      const int32_t r = j < j1 ? rlst[j] : -1;
+      if (r >= 0) {
+        my_pp = r >> 4;
+        my_nv = (r & 15) + 1;
+      }
+    } else {
+      int p = -1;
+      if (j < j1) p = lst ? ld_x<COH>(lst + j) : j;
+      if (p >= 0 && p < np) {
+        const int pp = pt_row[p];
+        if (pp >= 0 && pp < num_pages) {
+          my_pp = pp;
+          my_nv = min(kPage, L - p * kPage);
+        }
       }
     }
   }
-  auto page_of = [&](int j) -> PageRef {
+  // the page of wave-uniform j
+  __device__ __forceinline__ PageRef operator()(int j) const {
     PageRef pr{-1, 0};
     if (j >= j1) return pr;
     const int x = (j - j0 - wave) / NW;  // wave-uniform
@@ -155,7 +141,75 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     pr.pp = pp;
     pr.nv = min(kPage, L - p * kPage);
     return pr;
-  };
+  }
+};
+
+// Folds the NW waves' (max, sum, acc) of every query head, which every wave
+// has stored to sm.m / sm.l / sm.acc, into the workgroup's partial records
+// part[G][kPartStride].  COH: stored device-coherently; ENC: as (bits ^
+// kPartSentinel).  All threads call.
+template <int G, int NW, bool COH, bool ENC>
+__device__ __forceinline__ void put_partials(AttnSmem<G, NW>& sm, float* __restrict__ part) {
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += blockDim.x) {
+    const int g = idx / kHeadDim, dim = idx % kHeadDim;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
+    float a = 0.0f, ls = 0.0f;
+    if (M != -INFINITY) {
+#pragma unroll
+      for (int w = 0; w < NW; ++w) {
+        const float f = exp2f(sm.m[w][g] - M);
+        a = fmaf(sm.acc[w][g][dim], f, a);
+        ls = fmaf(sm.l[w][g], f, ls);
+      }
+    }
+    auto put = [&](int i, float x) {
+      if constexpr (ENC) st_x<COH>(reinterpret_cast<uint32_t*>(part) + i, __float_as_uint(x) ^ kPartSentinel);
+      else st_x<COH>(part + i, x);
+    };
+    put(g * kPartStride + dim, a);
+    if (dim == 0) {
+      put(g * kPartStride + kHeadDim, M);
+      put(g * kPartStride + kHeadDim + 1, ls);
+    }
+  }
+}
+
+// Attend to pages lst[j0 .. j1) (lst == nullptr: logical pages j0 .. j1) of
+// list (b, h) and write the workgroup's partial records to part[G][kPartStride].
+// rlst (optional; LDS or memory written before the launch) holds the pages
+// already resolved to (physical page << 4) | (valid tokens - 1), read with
+// plain loads; the page table is then not read.
+// PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
+// COH: lst is read and the partials are written device-coherently; ENC: the
+// partial words are stored as (bits ^ kPartSentinel).
+template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4, bool ENC = false>
+__device__ __forceinline__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
+                             const void* __restrict__ v, const uint16_t* __restrict__ ks,
+                             const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
+                             const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
+                             int j1, float scale_log2, float* __restrict__ part,
+                             AttnSmem<G, NW>& sm, const int32_t* rlst = nullptr) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int r = lane >> 4, c = lane & 15;
+  const int hq = hkv * G;
+
+  float qv[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) load8<QT>(q, ((size_t)b * hq + (size_t)h * G + g) * kHeadDim + 8 * c, qv[g]);
+
+  float m[G], l[G], acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    m[g] = -INFINITY;
+    l[g] = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+  }
+
+  const WavePages<COH, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages);
 
   for (int jb = j0 + wave; jb < j1; jb += NW * PW) {
     PageRef pg[PW];
@@ -243,31 +297,192 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
       }
     }
   }
-  __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += blockDim.x) {
-    const int g = idx / kHeadDim, dim = idx % kHeadDim;
-    float M = -INFINITY;
+  put_partials<G, NW, COH, ENC>(sm, part);
+}
+
+// ---------------------------------------------------------------- MFMA variant
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// Eight consecutive K elements of a row as one bf16 MFMA operand (int8 codes
+// are widened exactly: every code has at most 8 significant bits).
+template <int DT>
+struct KOp8;
+template <>
+struct KOp8<SA_BF16> {
+  uint4 w;
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+    w = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(base) + e);
+  }
+  __device__ __forceinline__ bf16x8_t get() const { return __builtin_bit_cast(bf16x8_t, w); }
+};
+template <>
+struct KOp8<SA_I8> {
+  uint2 w;
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+    w = *reinterpret_cast<const uint2*>(static_cast<const int8_t*>(base) + e);
+  }
+  __device__ __forceinline__ bf16x8_t get() const {
+    uint32_t o[4];
 #pragma unroll
-    for (int w = 0; w < NW; ++w) M = fmaxf(M, sm.m[w][g]);
-    float a = 0.0f, ls = 0.0f;
-    if (M != -INFINITY) {
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t word = i < 2 ? w.x : w.y;
+      const int sh = 16 * (i & 1);
+      const float lo = (float)(int8_t)(word >> sh), hi = (float)(int8_t)(word >> (sh + 8));
+      o[i] = (__float_as_uint(lo) >> 16) | (__float_as_uint(hi) & 0xFFFF0000u);
+    }
+    return __builtin_bit_cast(bf16x8_t, make_uint4(o[0], o[1], o[2], o[3]));
+  }
+};
+
+// Value of lane g of each 16-lane row (DPP row_newbcast).
+template <int g>
+__device__ __forceinline__ float row_bcast(float v) {
+  return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v),
+                                                               0x150 + g, 0xF, 0xF, false));
+}
+
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+// attend_range for G (<= 16) bf16 query heads per kv-head, with the scores
+// Q K^T of a page on the matrix cores: four v_mfma_f32_16x16x32_bf16 per page
+// compute the 16 tokens x 16 head-slots score tile (heads >= G are zero).
+// The A operand is the page's K: lane l supplies row l % 16 as token
+// 4 * (l % 4) + (l % 16) / 4 and 32 of its dimensions, (l / 16) * 32 .. + 31,
+// eight per MFMA; the B operand is Q^T laid out the same way.  With that token
+// order lane l ends up holding, for head l % 16, the scores of tokens
+// 4 i + l / 16 (i = 0..3): exactly the tokens whose V rows it holds in the
+// P V layout of attend_range (token row l / 16 of each group of four), so each
+// head's weights reach the P V lanes by one row broadcast from lane g of the
+// row, and P V stays on the vector ALUs in fp32 (no bf16 rounding of weights).
+// int8 K / V: the codes enter the MFMA exactly; the per-token scales multiply
+// the scores and the weights.  Partials as attend_range.
+template <int KT, int G, int NW = 4>
+__device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
+                                                  const void* __restrict__ k,
+                                                  const void* __restrict__ v,
+                                                  const uint16_t* __restrict__ ks,
+                                                  const uint16_t* __restrict__ vs, int num_pages,
+                                                  int hkv, int b, int h,
+                                                  const int32_t* __restrict__ pt_row, int L,
+                                                  const int32_t* lst, int j0, int j1,
+                                                  float scale_log2, float* __restrict__ part,
+                                                  AttnSmem<G, NW>& sm) {
+  static_assert(G >= 1 && G <= 16, "one MFMA column per query head");
+  static_assert(KT == SA_BF16 || KT == SA_I8, "K enters the MFMA as bf16");
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int n = lane & 15, qg = lane >> 4;  // MFMA column (head) and row group
+  const int r = qg, c = n;                  // P V layout: token row in a group of 4, dims 8c..
+  const int hq = hkv * G;
+  const int tok_a = 4 * (n & 3) + (n >> 2);  // the token of this lane's A row
+
+  bf16x8_t qb[4];
+  {
+    uint4 w[4] = {};
+    if (n < G) {
+      const uint4* qp = reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) +
+                                                       ((size_t)b * hq + (size_t)h * G + n) * kHeadDim +
+                                                       32 * qg);
 #pragma unroll
-      for (int w = 0; w < NW; ++w) {
-        const float f = exp2f(sm.m[w][g] - M);
-        a = fmaf(sm.acc[w][g][dim], f, a);
-        ls = fmaf(sm.l[w][g], f, ls);
+      for (int kk = 0; kk < 4; ++kk) w[kk] = qp[kk];
+    }
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) qb[kk] = __builtin_bit_cast(bf16x8_t, w[kk]);
+  }
+
+  float mrun = -INFINITY, lpart = 0.0f;  // head n: running max; this lane's tokens' weight sum
+  float acc[G][8];
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
+
+  const WavePages<false, NW> page_of(pt_row, lst, nullptr, j0, j1, L, num_pages);
+  for (int jb = j0 + wave; jb < j1; jb += NW) {
+    const PageRef pg = page_of(jb);
+    const size_t ppl = pg.pp >= 0 ? (size_t)pg.pp : 0;  // empty slot: load page 0, result unused
+    KOp8<KT> kr[4];
+    {
+      const size_t row = (ppl * kPage + tok_a) * hkv + h;
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk) kr[kk].load(k, row * kHeadDim + 32 * qg + 8 * kk);
+    }
+    Raw8<KT> vr[4];
+    float ksc[4], vsc[4];
+#pragma unroll
+    for (int it = 0; it < 4; ++it) {
+      const size_t tv = (ppl * kPage + 4 * it + r) * hkv + h;
+      vr[it].load(v, tv * kHeadDim + 8 * c);
+      if constexpr (KT == SA_I8) {
+        ksc[it] = f16_to_f32(ks[(ppl * kPage + 4 * it + qg) * hkv + h]);
+        vsc[it] = f16_to_f32(vs[tv]);
+      } else {
+        ksc[it] = vsc[it] = 1.0f;
       }
     }
-    auto put = [&](int i, float x) {
-      if constexpr (ENC) st_x<COH>(reinterpret_cast<uint32_t*>(part) + i, __float_as_uint(x) ^ kPartSentinel);
-      else st_x<COH>(part + i, x);
-    };
-    put(g * kPartStride + dim, a);
-    if (dim == 0) {
-      put(g * kPartStride + kHeadDim, M);
-      put(g * kPartStride + kHeadDim + 1, ls);
-    }
+    // every load of the page is issued before any of them is used
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk].get(), qb[kk], z, 0, 0, 0);
+
+    const bool live = pg.pp >= 0 && n < G;
+    float zz[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)  // token 4 i + qg
+      zz[i] = (live && 4 * i + qg < pg.nv) ? z[i] * (scale_log2 * ksc[i]) : -INFINITY;
+    float pm = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
+    pm = pair32_max(pair16_max(pm));  // over the page's 16 tokens, for head n
+    const float mn = fmaxf(mrun, pm);
+    const bool none = mn == -INFINITY;
+    const float alpha = none ? 1.0f : exp2f(mrun - mn);
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) p[i] = none ? 0.0f : exp2f(zz[i] - mn);
+    lpart = fmaf(lpart, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+    mrun = mn;
+
+    static_for<0, G>([&](auto gc) {
+      constexpr int g = decltype(gc)::value;
+      const float ag = row_bcast<g>(alpha);
+      float pw[4];
+#pragma unroll
+      for (int it = 0; it < 4; ++it) pw[it] = row_bcast<g>(p[it]) * vsc[it];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+#pragma unroll
+      for (int it = 0; it < 4; ++it) {
+        float vx[8];
+        vr[it].get(vx);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[it], vx[e], acc[g][e]);
+      }
+    });
   }
+
+  // fold the four token rows of each wave, then the NW waves
+  const float lsum = pair32_sum(pair16_sum(lpart));
+#pragma unroll
+  for (int g = 0; g < G; ++g)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) acc[g][e] = pair32_sum(pair16_sum(acc[g][e]));
+  if (qg == 0 && n < G) {
+    sm.m[wave][n] = mrun;
+    sm.l[wave][n] = lsum;
+  }
+  if (r == 0) {
+#pragma unroll
+    for (int g = 0; g < G; ++g)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sm.acc[wave][g][8 * c + e] = acc[g][e];
+  }
+  put_partials<G, NW, false, false>(sm, part);
 }
 
 // Merge ns partial records part[ns][G][kPartStride] of one list into
