@@ -35,21 +35,125 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
                                          scores + ((size_t)b * hkv + h) * max_pages);
 }
 
-// grid (ceil(max_units / units_per_wg), B), block 256
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kMfmaTilesPerWave = 2;                               // 16-page tiles in flight per wave
+constexpr int kMfmaPagesPerWG = 4 * kMfmaTilesPerWave * 16;        // 128 pages per workgroup
+
+// Quest scores of G (4..16) bf16 query heads over bf16 metadata on the matrix
+// cores: the bound of head g on a page is the dot product of [q_g+ | q_g-]
+// (256 values) with the page's [M | m] row pair (the 512 contiguous bytes of
+// its metadata), so a 16-page tile is the 16 x 16 product of [q+ | q-] (heads
+// as rows, G of 16 used) with the pages' rows as columns: eight
+// v_mfma_f32_16x16x32_bf16 over the 256-deep sum.  Lane l supplies, for MFMA
+// kk, elements 32 kk + 8 (l / 16) .. + 7 of head l % 16 (A) and of page l % 16
+// of the tile (B: one 16-byte load), so each lane loads its page's 128 bytes
+// as eight 16-byte pieces.  The result tile holds heads 4 (l / 16) + i of page
+// l % 16 in lane l; the group score is their max over the G heads.
+// grid (ceil(max_pages / 128), Hkv, B), block 256.
+template <int G>
+__global__ __launch_bounds__(256) void quest_score_mfma_kernel(
+    const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta, int num_pages, int hkv,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
+    float* __restrict__ scores) {
+  static_assert(G >= 4 && G <= 16, "heads fill the MFMA rows");
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int L = clamp_len(lens[b], max_pages);
+  const int n_valid = (L + kPage - 1) / kPage;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, kg = lane >> 4;
+  const int pw0 = blockIdx.x * kMfmaPagesPerWG + wave * kMfmaTilesPerWave * 16;
+  if (pw0 >= n_valid) return;
+  const int32_t* pt_row = pt + (size_t)b * max_pages;
+
+  // page-table entries and metadata of this wave's tiles: every load in flight at once
+  int pg[kMfmaTilesPerWave], pp[kMfmaTilesPerWave];
+#pragma unroll
+  for (int t = 0; t < kMfmaTilesPerWave; ++t) {
+    pg[t] = pw0 + 16 * t + col;
+    pp[t] = pt_row[min(pg[t], n_valid - 1)];
+  }
+  uint4 mw[kMfmaTilesPerWave][8];
+#pragma unroll
+  for (int t = 0; t < kMfmaTilesPerWave; ++t) {
+    const int ppl = (pp[t] >= 0 && pp[t] < num_pages) ? pp[t] : 0;
+    const uint4* row = reinterpret_cast<const uint4*>(meta + ((size_t)h * num_pages + ppl) * 2 * kHeadDim);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) mw[t][kk] = row[4 * kk + kg];
+  }
+  // A: [q+ | q-] of head col (zero beyond G): k < 128 takes q+ of dim k, k >= 128 q- of dim k - 128
+  uint4 aw[8] = {};
+  if (col < G) {
+    const uint4* qr = reinterpret_cast<const uint4*>(q + ((size_t)b * hkv * G + (size_t)h * G + col) * kHeadDim);
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk) {
+      const uint4 w = qr[(4 * kk + kg) & 15];
+      const bool neg_half = kk >= 4;  // the m row pairs with q-
+      uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const uint32_t neg = (x[e] & 0x8000u ? 0x0000FFFFu : 0u) | (x[e] & 0x80000000u ? 0xFFFF0000u : 0u);
+        x[e] &= neg_half ? neg : ~neg;
+      }
+      aw[kk] = make_uint4(x[0], x[1], x[2], x[3]);
+    }
+  }
+  float* sc_row = scores + ((size_t)b * hkv + h) * max_pages;
+#pragma unroll
+  for (int t = 0; t < kMfmaTilesPerWave; ++t) {
+    f32x4_t acc = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+    for (int kk = 0; kk < 8; ++kk)
+      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw[kk]),
+                                                   __builtin_bit_cast(bf16x8_t, mw[t][kk]), acc, 0, 0, 0);
+    float best = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (4 * kg + i < G) best = fmaxf(best, acc[i]);
+    best = pair32_max(pair16_max(best));
+    const bool ok = pg[t] < n_valid && pp[t] >= 0 && pp[t] < num_pages;
+    if (kg == 0 && pg[t] < n_valid) sc_row[pg[t]] = ok ? best : -INFINITY;
+  }
+}
+
+constexpr int kSalsUnitsPerWG = 8;  // blocks scored per workgroup, two per wave
+constexpr int kSalsHeads = 8;       // kv-heads of one pass over a block's tokens
+
+// Merge of two base-2 (max, sum) pairs; symmetric, so both partners of an
+// exchange end with bit-identical values.
+__device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2) {
+  const float mm = fmaxf(m, m2);
+  const float a = m == -INFINITY ? 0.0f : s * exp2f(m - mm);
+  const float c = m2 == -INFINITY ? 0.0f : s2 * exp2f(m2 - mm);
+  s = a + c;
+  m = mm;
+}
+
+// grid (ceil(max_units / kSalsUnitsPerWG), B), block 256.  The workgroup first
+// forms every kv-head's group-mean query in LDS and projects it, qt = qbar P,
+// on the matrix cores (fp32 v_mfma_f32_16x16x4f32, 16 kv-heads per tile).
+// Lane l then takes kv-head l % 8 of a group of kSalsHeads and token slot
+// l / 8: per 64-token pass it reads the page-table entries of its 8 tokens,
+// then their code words and scales (the 8 lanes of a slot read one token's
+// 64 contiguous bytes), and folds the 8 scores into a base-2 (max, sum).  The
+// 8 token slots of a kv-head are merged by three lane exchanges (xor 8, 16,
+// 32) at the end of the block.
 template <int QT>
 __global__ __launch_bounds__(256) void sals_score_kernel(
     const void* __restrict__ q, int hq, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const float* __restrict__ proj, int num_pages, int hkv,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
-    int unit_tokens, float tau_log2e, float* __restrict__ scores, int max_units,
-    int units_per_wg) {
+    int unit_tokens, float tau_log2e, float* __restrict__ scores, int max_units) {
+  typedef float f32x4 __attribute__((ext_vector_type(4)));
   __shared__ float qbar[64 * kHeadDim];  // [hkv][d] group-mean query (hkv <= 64)
   __shared__ float qt_s[64 * kRank];     // [hkv][rank] projected index query
   const int b = blockIdx.y;
   const int L = clamp_len(lens[b], max_pages);
   const int nu = (L + unit_tokens - 1) / unit_tokens;
-  const int u0 = blockIdx.x * units_per_wg;
+  const int u0 = blockIdx.x * kSalsUnitsPerWG;
   if (u0 >= nu) return;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int G = hq / hkv;
   const float inv_g = 1.0f / (float)G;
   for (int i = threadIdx.x; i < hkv * kHeadDim; i += blockDim.x) {
@@ -63,60 +167,94 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
     qbar[i] = s * inv_g;
   }
   __syncthreads();
-  for (int i = threadIdx.x; i < hkv * kRank; i += blockDim.x) {
-    const int hh = i / kRank, j = i % kRank;
-    float s = 0.0f;
-    for (int dim = 0; dim < kHeadDim; ++dim) s = fmaf(qbar[hh * kHeadDim + dim], proj[dim * kRank + j], s);
-    qt_s[i] = s;
+  for (int t = wave; t * 16 < hkv; t += 4) {  // qt rows 16 t .. 16 t + 15
+    const int m = 16 * t + (lane & 15);
+    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll 8
+    for (int kk = 0; kk < kHeadDim / 4; ++kk) {
+      const int kx = 4 * kk + (lane >> 4);
+      const float av = m < hkv ? qbar[m * kHeadDim + kx] : 0.0f;
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, proj[kx * kRank + (lane & 15)], c, 0, 0, 0);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int row = 16 * t + 4 * (lane >> 4) + i;
+      if (row < hkv) qt_s[row * kRank + (lane & 15)] = c[i];
+    }
   }
   __syncthreads();
 
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int tpl = 64 / hkv;  // tokens per 64-lane load
-  const int tl = lane / hkv, hh = lane % hkv;
-  float qt[kRank];
+  const int x = lane & (kSalsHeads - 1), ts = lane / kSalsHeads;
+  const int32_t* pt_b = pt + (size_t)b * max_pages;
+  const uint2* cw_base = reinterpret_cast<const uint2*>(codes);
+  const int u_end = min(u0 + kSalsUnitsPerWG, nu);
+  for (int h0 = 0; h0 < hkv; h0 += kSalsHeads) {
+    const bool hv = h0 + x < hkv;
+    const int hh = hv ? h0 + x : h0;
+    float qt[kRank];
 #pragma unroll
-  for (int j = 0; j < kRank; ++j) qt[j] = qt_s[hh * kRank + j];
-
-  const int u_end = min(u0 + units_per_wg, nu);
-  for (int u = u0 + wave; u < u_end; u += 4) {
-    const int t_begin = u * unit_tokens;
-    const int t_end = min(t_begin + unit_tokens, L);
-    float m = -INFINITY, s = 0.0f;
-    for (int t0 = t_begin; t0 < t_end; t0 += tpl) {
-      const int t = t0 + tl;
-      if (t < t_end) {
-        const int pp = pt[(size_t)b * max_pages + (t >> 4)];
-        if (pp >= 0 && pp < num_pages) {
-          const size_t row = ((size_t)pp * kPage + (t & 15)) * hkv + hh;
-          const uint2 w = *reinterpret_cast<const uint2*>(codes + row * (kRank / 2));
-          const float sc = f16_to_f32(scales[row]);
+    for (int j = 0; j < kRank; ++j) qt[j] = qt_s[hh * kRank + j];
+    for (int u = u0 + wave; u < u_end; u += 4) {
+      float m = -INFINITY, s = 0.0f;
+      for (int t0 = 0; t0 < unit_tokens; t0 += 64) {
+        int pp[8], tok[8];
+        bool in[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          const int to = t0 + ts + 8 * i;
+          tok[i] = u * unit_tokens + to;
+          in[i] = to < unit_tokens && tok[i] < L;
+          pp[i] = pt_b[in[i] ? tok[i] >> 4 : 0];
+        }
+        uint2 cw[8];
+        uint16_t sw[8];
+        bool ok[8];
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+          ok[i] = in[i] && pp[i] >= 0 && pp[i] < num_pages;
+          const size_t row = ((size_t)(ok[i] ? pp[i] : 0) * kPage + (tok[i] & 15)) * hkv + hh;
+          cw[i] = cw_base[row];
+          sw[i] = scales[row];
+        }
+        float z[8], zmax = -INFINITY;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
           float dot = 0.0f;
 #pragma unroll
           for (int j = 0; j < kRank; ++j) {
-            const uint32_t word = j < 8 ? w.x : w.y;
-            const int cj = (int)(word << (28 - 4 * (j & 7))) >> 28;
-            dot = fmaf(qt[j], (float)cj, dot);
+            const uint32_t word = j < 8 ? cw[i].x : cw[i].y;
+            dot = fmaf(qt[j], (float)((int)(word << (28 - 4 * (j & 7))) >> 28), dot);
           }
-          const float z = tau_log2e * (sc * dot);
-          if (z > m) {
-            s = s * exp2f(m - z) + 1.0f;
-            m = z;
-          } else {
-            s += exp2f(z - m);
-          }
+          z[i] = (ok[i] && hv) ? tau_log2e * (f16_to_f32(sw[i]) * dot) : -INFINITY;
+          zmax = fmaxf(zmax, z[i]);
+        }
+        if (zmax != -INFINITY) {
+          float sc = 0.0f;
+#pragma unroll
+          for (int i = 0; i < 8; ++i) sc += z[i] == -INFINITY ? 0.0f : exp2f(z[i] - zmax);
+          lse_merge(m, s, zmax, sc);
         }
       }
+      // the 8 token slots of kv-head x: lanes x + 8 k
+      lse_merge(m, s, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(m), 0x128, 0xF, 0xF, false)),
+                __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(s), 0x128, 0xF, 0xF, false)));
+      {
+        const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+        m = __uint_as_float(rm[0]);
+        s = __uint_as_float(rs[0]);
+        lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+      }
+      {
+        const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
+        const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
+        m = __uint_as_float(rm[0]);
+        s = __uint_as_float(rs[0]);
+        lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+      }
+      if (ts == 0 && hv)
+        scores[((size_t)b * hkv + h0 + x) * max_units + u] = m == -INFINITY ? -INFINITY : (m + __log2f(s)) * kLn2;
     }
-    // merge (m, s) over the lanes that hold the same kv-head
-    for (int mask = hkv; mask < 64; mask <<= 1) {
-      const float m2 = __shfl_xor(m, mask, 64);
-      const float s2 = __shfl_xor(s, mask, 64);
-      const float mm = fmaxf(m, m2);
-      s = (mm == -INFINITY) ? 0.0f : s * exp2f(m - mm) + s2 * exp2f(m2 - mm);
-      m = mm;
-    }
-    if (tl == 0) scores[((size_t)b * hkv + hh) * max_units + u] = (m + __log2f(s)) * kLn2;
   }
 }
 
@@ -148,6 +286,21 @@ hipError_t launch_quest_score(int kv_dtype, int q_dtype, const void* q, const vo
   if (kv_dtype == SA_F32)
     return q_dtype == SA_F32 ? quest_dispatch_g<SA_F32, SA_F32>(G, grid, st, q, meta, s, pt, lens, scores)
                              : quest_dispatch_g<SA_F32, SA_BF16>(G, grid, st, q, meta, s, pt, lens, scores);
+  if (q_dtype == SA_BF16 && G >= 4) {  // bf16 query groups of four or more: matrix cores
+    const dim3 gm((s.max_pages + kMfmaPagesPerWG - 1) / kMfmaPagesPerWG, s.Hkv, s.B);
+    const uint16_t* qh = static_cast<const uint16_t*>(q);
+    const uint16_t* mh = static_cast<const uint16_t*>(meta);
+#define SA_QM(GG)                                                                               \
+  hipLaunchKernelGGL((quest_score_mfma_kernel<GG>), gm, dim3(256), 0, st, qh, mh, s.num_pages, \
+                     s.Hkv, pt, lens, s.max_pages, scores)
+    switch (G) {
+      case 4: SA_QM(4); break;
+      case 8: SA_QM(8); break;
+      default: SA_QM(16); break;
+    }
+#undef SA_QM
+    return hipGetLastError();
+  }
   return q_dtype == SA_F32 ? quest_dispatch_g<SA_BF16, SA_F32>(G, grid, st, q, meta, s, pt, lens, scores)
                            : quest_dispatch_g<SA_BF16, SA_BF16>(G, grid, st, q, meta, s, pt, lens, scores);
 }
@@ -156,17 +309,16 @@ hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,
                              const uint16_t* scales, const float* proj, const Shapes& s,
                              const int32_t* pt, const int32_t* lens, int unit_tokens, float tau,
                              float* scores, int max_units, hipStream_t st) {
-  const int upw = 8;
-  dim3 grid((max_units + upw - 1) / upw, s.B);
+  dim3 grid((max_units + kSalsUnitsPerWG - 1) / kSalsUnitsPerWG, s.B);
   const float tl2 = tau * kLog2e;
   if (q_dtype == SA_F32)
     hipLaunchKernelGGL(sals_score_kernel<SA_F32>, grid, dim3(256), 0, st, q, s.Hq, codes, scales,
                        proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2, scores,
-                       max_units, upw);
+                       max_units);
   else
     hipLaunchKernelGGL(sals_score_kernel<SA_BF16>, grid, dim3(256), 0, st, q, s.Hq, codes, scales,
                        proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2, scores,
-                       max_units, upw);
+                       max_units);
   return hipGetLastError();
 }
 
