@@ -37,15 +37,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
                             lst, j0, j1, scale_log2, part, sm);
 }
 
-// grid (Hkv, B), block 256: merge the splits of one list
+// grid (G, Hkv, B), block 256: merge the splits of one query head of one list
+// (two thread groups of 128 outputs, each folding half of the splits)
 __global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __restrict__ partials,
                                                             int hkv, int G, int nsplit,
                                                             float* __restrict__ out) {
   __shared__ float lds[3 * kAttnThreads];
-  const int h = blockIdx.x, b = blockIdx.y;
+  const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
   const size_t list = (size_t)b * hkv + h;
   merge_list(partials + list * nsplit * G * kPartStride, nsplit, G,
-             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, lds);
+             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, lds, nullptr, g, 1);
 }
 
 template <int KT, int QT>
@@ -109,8 +110,8 @@ hipError_t launch_attention(int kv_dtype, int q_dtype, const void* q, const void
   }
 #undef SA_KQ
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(s.Hkv, s.B), dim3(kAttnThreads), 0, st, partials, s.Hkv, G,
-                     plan.nsplit, out);
+  hipLaunchKernelGGL(merge_kernel, dim3(G, s.Hkv, s.B), dim3(kAttnThreads), 0, st, partials, s.Hkv,
+                     G, plan.nsplit, out);
   return hipGetLastError();
 }
 

@@ -486,8 +486,9 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 }
 
 // Merge ns partial records part[ns][G][kPartStride] of one list into
-// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).  The
-// workgroup's threads form P = blockDim / (G * 128) groups (at least one);
+// out[G][128]: out = sum_s acc_s 2^(m_s - M) / sum_s l_s 2^(m_s - M), for the
+// query heads g0 .. g0 + gn - 1 (gn < 0: all G).  The workgroup's threads
+// form P = blockDim / (gn * 128) groups (at least one);
 // group p folds splits p, p + P, p + 2P, ... into a running (M, acc, sum),
 // fetching C splits per memory round trip, and the groups are combined
 // through lds (3 * blockDim floats).  The order is fixed, so the result is
@@ -498,13 +499,15 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 template <bool COH = false, bool ENC = false, int C = 16>
 __device__ __forceinline__ void merge_list(const float* __restrict__ part, int ns, int G,
                                            float* __restrict__ out, float* __restrict__ lds,
-                                           uint32_t* err = nullptr) {
-  const int no = G * kHeadDim;
+                                           uint32_t* err = nullptr, int g0 = 0, int gn = -1) {
+  if (gn < 0) gn = G;
+  out += (size_t)g0 * kHeadDim;
+  const int no = gn * kHeadDim;
   const int nt = blockDim.x;
   const int P = nt / no > 1 ? nt / no : 1;
   // folds splits first, first + step, ... (< ns) of output o into (M, a, lsum)
   auto fold = [&](int o, int first, int step, float& M, float& a, float& lsum) {
-    const int g = o / kHeadDim, dim = o % kHeadDim;
+    const int g = g0 + o / kHeadDim, dim = o % kHeadDim;
     for (int s0 = first; s0 < ns; s0 += C * step) {
       float av[C], mv[C], lv[C];
       if constexpr (ENC) {
