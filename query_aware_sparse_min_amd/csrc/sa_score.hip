@@ -118,6 +118,10 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 }
 
 constexpr int kSalsUnitsPerWG = 8;  // blocks scored per workgroup, two per wave
+constexpr int kQbarStride = kHeadDim + 4;  // padded rows: the MFMA reads 16 rows at one column
+__host__ __device__ constexpr size_t sals_smem_bytes(int hkv) {
+  return sizeof(float) * ((size_t)kHeadDim * kRank + (size_t)hkv * kQbarStride + (size_t)hkv * kRank);
+}
 constexpr int kSalsHeads = 8;       // kv-heads of one pass over a block's tokens
 
 // Merge of two base-2 (max, sum) pairs; symmetric, so both partners of an
@@ -131,14 +135,15 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 }
 
 // grid (ceil(max_units / kSalsUnitsPerWG), B), block 256.  The workgroup first
-// forms every kv-head's group-mean query in LDS and projects it, qt = qbar P,
-// on the matrix cores (fp32 v_mfma_f32_16x16x4f32, 16 kv-heads per tile).
-// Lane l then takes kv-head l % 8 of a group of kSalsHeads and token slot
-// l / 8: per 64-token pass it reads the page-table entries of its 8 tokens,
-// then their code words and scales (the 8 lanes of a slot read one token's
-// 64 contiguous bytes), and folds the 8 scores into a base-2 (max, sum).  The
-// 8 token slots of a kv-head are merged by three lane exchanges (xor 8, 16,
-// 32) at the end of the block.
+// stages the batch row of q and the projection P in LDS (vector loads, one
+// memory round trip), forms every kv-head's group-mean query and projects it,
+// qt = qbar P, on the matrix cores (fp32 v_mfma_f32_16x16x4f32, 16 kv-heads
+// per tile).  Lane l then takes kv-head l % 8 of a group of kSalsHeads and
+// token slot l / 8; a wave scores its two blocks together: per 64-token pass it
+// reads the page-table entries of its 16 tokens, then their code words and
+// scales (the 8 lanes of a slot read one token's 64 contiguous bytes), and
+// folds each block's 8 scores per lane into a base-2 (max, sum).  The 8 token
+// slots of a kv-head are merged by three lane exchanges (xor 8, 16, 32).
 template <int QT>
 __global__ __launch_bounds__(256) void sals_score_kernel(
     const void* __restrict__ q, int hq, const uint8_t* __restrict__ codes,
@@ -146,26 +151,92 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
     int unit_tokens, float tau_log2e, float* __restrict__ scores, int max_units) {
   typedef float f32x4 __attribute__((ext_vector_type(4)));
-  __shared__ float qbar[64 * kHeadDim];  // [hkv][d] group-mean query (hkv <= 64)
-  __shared__ float qt_s[64 * kRank];     // [hkv][rank] projected index query
+  extern __shared__ float sals_smem[];   // sized by sals_smem_bytes(hkv)
+  float* proj_s = sals_smem;                      // [d][rank]
+  float* qbar = proj_s + kHeadDim * kRank;        // [hkv][kQbarStride] group-mean query
+  float* qt_s = qbar + hkv * kQbarStride;         // [hkv][rank] projected index query
   const int b = blockIdx.y;
   const int L = clamp_len(lens[b], max_pages);
   const int nu = (L + unit_tokens - 1) / unit_tokens;
   const int u0 = blockIdx.x * kSalsUnitsPerWG;
   if (u0 >= nu) return;
-  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int G = hq / hkv;
-  const float inv_g = 1.0f / (float)G;
-  for (int i = threadIdx.x; i < hkv * kHeadDim; i += blockDim.x) {
-    const int hh = i / kHeadDim, dim = i % kHeadDim;
-    float s = 0.0f;
-    for (int g = 0; g < G; ++g) {
-      const size_t qi = ((size_t)b * hq + (size_t)hh * G + g) * kHeadDim + dim;
-      s += QT == SA_F32 ? static_cast<const float*>(q)[qi]
-                        : bf16_to_f32(static_cast<const uint16_t*>(q)[qi]);
+  const int x = lane & (kSalsHeads - 1), ts = lane / kSalsHeads;
+  const int32_t* pt_b = pt + (size_t)b * max_pages;
+  const uint2* cw_base = reinterpret_cast<const uint2*>(codes);
+  const int u_end = min(u0 + kSalsUnitsPerWG, nu);
+  const int ua = u0 + wave;  // the wave's two blocks: ua and ua + 4
+
+  // one pass = 64 tokens of both blocks for one group of kSalsHeads kv-heads
+  int pp[16], tok[16];
+  bool in[16], ok[16];
+  uint2 cw[16];
+  uint16_t sw[16];
+  auto issue_pt = [&](int t0) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const int u = ua + 4 * (i / 8);
+      const int to = t0 + ts + 8 * (i % 8);
+      tok[i] = u * unit_tokens + to;
+      in[i] = u < u_end && to < unit_tokens && tok[i] < L;
+      pp[i] = pt_b[in[i] ? tok[i] >> 4 : 0];
     }
-    qbar[i] = s * inv_g;
+  };
+  auto issue_codes = [&](int hh) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      ok[i] = in[i] && pp[i] >= 0 && pp[i] < num_pages;
+      const size_t row = ((size_t)(ok[i] ? pp[i] : 0) * kPage + (tok[i] & 15)) * hkv + hh;
+      cw[i] = cw_base[row];
+      sw[i] = scales[row];
+    }
+  };
+  // the first pass's page-table entries, then (below) its codes, are in flight
+  // while the index query is formed
+  issue_pt(0);
+
+  // P into LDS and the group means of q (four dimensions of one kv-head per
+  // thread and pass, its G query rows loaded at once), all in one round trip
+  {
+    constexpr int kP4 = kHeadDim * kRank / 4 / 256;
+    float4 pv[kP4];
+#pragma unroll
+    for (int r = 0; r < kP4; ++r) pv[r] = reinterpret_cast<const float4*>(proj)[tid + 256 * r];
+    const float inv_g = 1.0f / (float)G;
+    for (int pi = tid; pi < hkv * (kHeadDim / 4); pi += 256) {
+      const int hh = pi / (kHeadDim / 4), d0 = 4 * (pi % (kHeadDim / 4));
+      float4 qv[16];
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        const size_t qi = ((size_t)b * hq + (size_t)hh * G + min(g, G - 1)) * kHeadDim + d0;
+        if constexpr (QT == SA_F32) {
+          qv[g] = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + qi);
+        } else {
+          const uint2 w = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + qi);
+          qv[g] = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
+        }
+      }
+      float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+#pragma unroll
+      for (int g = 0; g < 16; ++g) {
+        if (g < G) {
+          sum.x += qv[g].x;
+          sum.y += qv[g].y;
+          sum.z += qv[g].z;
+          sum.w += qv[g].w;
+        }
+      }
+      float* dst = qbar + hh * kQbarStride + d0;
+      dst[0] = sum.x * inv_g;
+      dst[1] = sum.y * inv_g;
+      dst[2] = sum.z * inv_g;
+      dst[3] = sum.w * inv_g;
+    }
+#pragma unroll
+    for (int r = 0; r < kP4; ++r) reinterpret_cast<float4*>(proj_s)[tid + 256 * r] = pv[r];
   }
+  issue_codes(x < hkv ? x : 0);
   __syncthreads();
   for (int t = wave; t * 16 < hkv; t += 4) {  // qt rows 16 t .. 16 t + 15
     const int m = 16 * t + (lane & 15);
@@ -173,8 +244,8 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
 #pragma unroll 8
     for (int kk = 0; kk < kHeadDim / 4; ++kk) {
       const int kx = 4 * kk + (lane >> 4);
-      const float av = m < hkv ? qbar[m * kHeadDim + kx] : 0.0f;
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, proj[kx * kRank + (lane & 15)], c, 0, 0, 0);
+      const float av = m < hkv ? qbar[m * kQbarStride + kx] : 0.0f;
+      c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, proj_s[kx * kRank + (lane & 15)], c, 0, 0, 0);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -184,76 +255,64 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
   }
   __syncthreads();
 
-  const int x = lane & (kSalsHeads - 1), ts = lane / kSalsHeads;
-  const int32_t* pt_b = pt + (size_t)b * max_pages;
-  const uint2* cw_base = reinterpret_cast<const uint2*>(codes);
-  const int u_end = min(u0 + kSalsUnitsPerWG, nu);
   for (int h0 = 0; h0 < hkv; h0 += kSalsHeads) {
     const bool hv = h0 + x < hkv;
     const int hh = hv ? h0 + x : h0;
     float qt[kRank];
 #pragma unroll
     for (int j = 0; j < kRank; ++j) qt[j] = qt_s[hh * kRank + j];
-    for (int u = u0 + wave; u < u_end; u += 4) {
-      float m = -INFINITY, s = 0.0f;
-      for (int t0 = 0; t0 < unit_tokens; t0 += 64) {
-        int pp[8], tok[8];
-        bool in[8];
+    float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.0f, 0.0f};
+    for (int t0 = 0; t0 < unit_tokens; t0 += 64) {
+      if (h0 > 0 || t0 > 0) {  // the first pass was fetched ahead
+        issue_pt(t0);
+        issue_codes(hh);
+      }
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          const int to = t0 + ts + 8 * i;
-          tok[i] = u * unit_tokens + to;
-          in[i] = to < unit_tokens && tok[i] < L;
-          pp[i] = pt_b[in[i] ? tok[i] >> 4 : 0];
-        }
-        uint2 cw[8];
-        uint16_t sw[8];
-        bool ok[8];
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-          ok[i] = in[i] && pp[i] >= 0 && pp[i] < num_pages;
-          const size_t row = ((size_t)(ok[i] ? pp[i] : 0) * kPage + (tok[i] & 15)) * hkv + hh;
-          cw[i] = cw_base[row];
-          sw[i] = scales[row];
-        }
+      for (int blk = 0; blk < 2; ++blk) {
         float z[8], zmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
+          const int ii = 8 * blk + i;
           float dot = 0.0f;
 #pragma unroll
           for (int j = 0; j < kRank; ++j) {
-            const uint32_t word = j < 8 ? cw[i].x : cw[i].y;
+            const uint32_t word = j < 8 ? cw[ii].x : cw[ii].y;
             dot = fmaf(qt[j], (float)((int)(word << (28 - 4 * (j & 7))) >> 28), dot);
           }
-          z[i] = (ok[i] && hv) ? tau_log2e * (f16_to_f32(sw[i]) * dot) : -INFINITY;
+          z[i] = (ok[ii] && hv) ? tau_log2e * (f16_to_f32(sw[ii]) * dot) : -INFINITY;
           zmax = fmaxf(zmax, z[i]);
         }
         if (zmax != -INFINITY) {
           float sc = 0.0f;
 #pragma unroll
           for (int i = 0; i < 8; ++i) sc += z[i] == -INFINITY ? 0.0f : exp2f(z[i] - zmax);
-          lse_merge(m, s, zmax, sc);
+          lse_merge(m[blk], s[blk], zmax, sc);
         }
       }
+    }
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
       // the 8 token slots of kv-head x: lanes x + 8 k
-      lse_merge(m, s, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(m), 0x128, 0xF, 0xF, false)),
-                __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(s), 0x128, 0xF, 0xF, false)));
+      float mb = m[blk], sb = s[blk];
+      lse_merge(mb, sb, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(mb), 0x128, 0xF, 0xF, false)),
+                __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(sb), 0x128, 0xF, 0xF, false)));
       {
-        const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-        m = __uint_as_float(rm[0]);
-        s = __uint_as_float(rs[0]);
-        lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+        const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
+        const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(sb), __float_as_uint(sb), false, false);
+        mb = __uint_as_float(rm[0]);
+        sb = __uint_as_float(rs[0]);
+        lse_merge(mb, sb, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
       }
       {
-        const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(m), __float_as_uint(m), false, false);
-        const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(s), __float_as_uint(s), false, false);
-        m = __uint_as_float(rm[0]);
-        s = __uint_as_float(rs[0]);
-        lse_merge(m, s, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
+        const auto rm = __builtin_amdgcn_permlane32_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
+        const auto rs = __builtin_amdgcn_permlane32_swap(__float_as_uint(sb), __float_as_uint(sb), false, false);
+        mb = __uint_as_float(rm[0]);
+        sb = __uint_as_float(rs[0]);
+        lse_merge(mb, sb, __uint_as_float(rm[1]), __uint_as_float(rs[1]));
       }
-      if (ts == 0 && hv)
-        scores[((size_t)b * hkv + h0 + x) * max_units + u] = m == -INFINITY ? -INFINITY : (m + __log2f(s)) * kLn2;
+      const int u = ua + 4 * blk;
+      if (ts == 0 && hv && u < u_end)
+        scores[((size_t)b * hkv + h0 + x) * max_units + u] = mb == -INFINITY ? -INFINITY : (mb + __log2f(sb)) * kLn2;
     }
   }
 }
@@ -311,12 +370,13 @@ hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,
                              float* scores, int max_units, hipStream_t st) {
   dim3 grid((max_units + kSalsUnitsPerWG - 1) / kSalsUnitsPerWG, s.B);
   const float tl2 = tau * kLog2e;
+  const size_t smem = sals_smem_bytes(s.Hkv);
   if (q_dtype == SA_F32)
-    hipLaunchKernelGGL(sals_score_kernel<SA_F32>, grid, dim3(256), 0, st, q, s.Hq, codes, scales,
+    hipLaunchKernelGGL(sals_score_kernel<SA_F32>, grid, dim3(256), smem, st, q, s.Hq, codes, scales,
                        proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2, scores,
                        max_units);
   else
-    hipLaunchKernelGGL(sals_score_kernel<SA_BF16>, grid, dim3(256), 0, st, q, s.Hq, codes, scales,
+    hipLaunchKernelGGL(sals_score_kernel<SA_BF16>, grid, dim3(256), smem, st, q, s.Hq, codes, scales,
                        proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2, scores,
                        max_units);
   return hipGetLastError();
