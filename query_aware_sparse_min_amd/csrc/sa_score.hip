@@ -119,8 +119,11 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 
 constexpr int kSalsUnitsPerWG = 8;  // blocks scored per workgroup, two per wave
 constexpr int kQbarStride = kHeadDim + 4;  // padded rows: the MFMA reads 16 rows at one column
+constexpr int kQDigits = 6;         // balanced base-16 digits of the fixed-point index query
+constexpr int kQFracBits = 22;      // |Q| < 2^22 (six balanced digits reach 7.8e6)
 __host__ __device__ constexpr size_t sals_smem_bytes(int hkv) {
-  return sizeof(float) * ((size_t)kHeadDim * kRank + (size_t)hkv * kQbarStride + (size_t)hkv * kRank);
+  return sizeof(float) * ((size_t)kHeadDim * kRank + (size_t)hkv * kQbarStride) +
+         sizeof(uint32_t) * (size_t)hkv * (2 * kQDigits + 1);
 }
 constexpr int kSalsHeads = 8;       // kv-heads of one pass over a block's tokens
 
@@ -138,14 +141,19 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 // stages the batch row of q and the projection P in LDS (vector loads, one
 // memory round trip), forms every kv-head's group-mean query and projects it,
 // qt = qbar P, on the matrix cores (fp32 v_mfma_f32_16x16x4f32, 16 kv-heads
-// per tile).  Lane l then takes kv-head l % 8 of a group of kSalsHeads and
+// per tile).  Each kv-head's qt becomes integers Q_j = rint(qt_j 2^(22-e)),
+// 2^(e-1) <= max |qt_j| < 2^e, written as six balanced base-16 digits packed
+// as signed nibbles; a token's dot product with its sixteen int4 codes is then
+// exact integer work (twelve v_dot8_i32_i4, Horner over the digits), scaled by
+// 2^(e-22).  Lane l then takes kv-head l % 8 of a group of kSalsHeads and
 // token slot l / 8; a wave scores its two blocks together: per 64-token pass it
 // reads the page-table entries of its 16 tokens, then their code words and
 // scales (the 8 lanes of a slot read one token's 64 contiguous bytes), and
 // folds each block's 8 scores per lane into a base-2 (max, sum).  The 8 token
 // slots of a kv-head are merged by three lane exchanges (xor 8, 16, 32).
-template <int QT>
-__global__ __launch_bounds__(256) void sals_score_kernel(
+// (sixteen query rows of fp32 need more registers: three waves per SIMD)
+template <int QT, int G>
+__global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
     const void* __restrict__ q, int hq, const uint8_t* __restrict__ codes,
     const uint16_t* __restrict__ scales, const float* __restrict__ proj, int num_pages, int hkv,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
@@ -154,14 +162,16 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
   extern __shared__ float sals_smem[];   // sized by sals_smem_bytes(hkv)
   float* proj_s = sals_smem;                      // [d][rank]
   float* qbar = proj_s + kHeadDim * kRank;        // [hkv][kQbarStride] group-mean query
-  float* qt_s = qbar + hkv * kQbarStride;         // [hkv][rank] projected index query
+  // [hkv][kQDigits][2] digit words of the projected index query (columns 0-7,
+  // 8-15), then [hkv] scales 2^(e-22)
+  uint32_t* qd_s = reinterpret_cast<uint32_t*>(qbar + hkv * kQbarStride);
+  float* qf_s = reinterpret_cast<float*>(qd_s + hkv * 2 * kQDigits);
   const int b = blockIdx.y;
   const int L = clamp_len(lens[b], max_pages);
   const int nu = (L + unit_tokens - 1) / unit_tokens;
   const int u0 = blockIdx.x * kSalsUnitsPerWG;
   if (u0 >= nu) return;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int G = hq / hkv;
   const int x = lane & (kSalsHeads - 1), ts = lane / kSalsHeads;
   const int32_t* pt_b = pt + (size_t)b * max_pages;
   const uint2* cw_base = reinterpret_cast<const uint2*>(codes);
@@ -196,20 +206,20 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
   // while the index query is formed
   issue_pt(0);
 
-  // P into LDS and the group means of q (four dimensions of one kv-head per
-  // thread and pass, its G query rows loaded at once), all in one round trip
+  // P and the group means of q into LDS: four dimensions of one kv-head per
+  // thread and item, its G query rows loaded at once, in the same round trip
+  // as the page-table entries.  The codes of the first pass are issued next,
+  // so they are in flight while qt is formed.
   {
     constexpr int kP4 = kHeadDim * kRank / 4 / 256;
-    float4 pv[kP4];
-#pragma unroll
-    for (int r = 0; r < kP4; ++r) pv[r] = reinterpret_cast<const float4*>(proj)[tid + 256 * r];
+    constexpr int kItemsPerHead = kHeadDim / 4;
+    const int n_items = hkv * kItemsPerHead;
     const float inv_g = 1.0f / (float)G;
-    for (int pi = tid; pi < hkv * (kHeadDim / 4); pi += 256) {
-      const int hh = pi / (kHeadDim / 4), d0 = 4 * (pi % (kHeadDim / 4));
-      float4 qv[16];
+    auto load_item = [&](int pi, float4 (&qv)[G]) {
+      const int hh = pi / kItemsPerHead, d0 = 4 * (pi % kItemsPerHead);
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        const size_t qi = ((size_t)b * hq + (size_t)hh * G + min(g, G - 1)) * kHeadDim + d0;
+      for (int g = 0; g < G; ++g) {
+        const size_t qi = ((size_t)b * hq + (size_t)hh * G + g) * kHeadDim + d0;
         if constexpr (QT == SA_F32) {
           qv[g] = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + qi);
         } else {
@@ -217,40 +227,84 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
           qv[g] = make_float4(bf16_lo(w.x), bf16_hi(w.x), bf16_lo(w.y), bf16_hi(w.y));
         }
       }
-      float4 sum = make_float4(0.0f, 0.0f, 0.0f, 0.0f);
+    };
+    auto store_item = [&](int pi, const float4 (&qv)[G]) {
+      float4 sum = qv[0];
 #pragma unroll
-      for (int g = 0; g < 16; ++g) {
-        if (g < G) {
-          sum.x += qv[g].x;
-          sum.y += qv[g].y;
-          sum.z += qv[g].z;
-          sum.w += qv[g].w;
-        }
+      for (int g = 1; g < G; ++g) {
+        sum.x += qv[g].x;
+        sum.y += qv[g].y;
+        sum.z += qv[g].z;
+        sum.w += qv[g].w;
       }
-      float* dst = qbar + hh * kQbarStride + d0;
+      float* dst = qbar + (pi / kItemsPerHead) * kQbarStride + 4 * (pi % kItemsPerHead);
       dst[0] = sum.x * inv_g;
       dst[1] = sum.y * inv_g;
       dst[2] = sum.z * inv_g;
       dst[3] = sum.w * inv_g;
-    }
+    };
+    float4 pv[kP4];
+#pragma unroll
+    for (int r = 0; r < kP4; ++r) pv[r] = reinterpret_cast<const float4*>(proj)[tid + 256 * r];
+    float4 qv[G];
+    if (tid < n_items) load_item(tid, qv);
 #pragma unroll
     for (int r = 0; r < kP4; ++r) reinterpret_cast<float4*>(proj_s)[tid + 256 * r] = pv[r];
+    if (tid < n_items) store_item(tid, qv);
+    for (int pi = tid + 256; pi < n_items; pi += 256) {
+      load_item(pi, qv);
+      store_item(pi, qv);
+    }
   }
+  // nothing above may sink below the code loads: a load issued after them
+  // would wait for them (memory counters retire in order)
+  __builtin_amdgcn_sched_barrier(0);
   issue_codes(x < hkv ? x : 0);
   __syncthreads();
   for (int t = wave; t * 16 < hkv; t += 4) {  // qt rows 16 t .. 16 t + 15
-    const int m = 16 * t + (lane & 15);
-    f32x4 c = {0.0f, 0.0f, 0.0f, 0.0f};
+    // rows past hkv repeat the last kv-head; their results are not used
+    const int m = min(16 * t + (lane & 15), hkv - 1);
+    f32x4 c2[2] = {{0.0f, 0.0f, 0.0f, 0.0f}, {0.0f, 0.0f, 0.0f, 0.0f}};
 #pragma unroll 8
     for (int kk = 0; kk < kHeadDim / 4; ++kk) {
       const int kx = 4 * kk + (lane >> 4);
-      const float av = m < hkv ? qbar[m * kQbarStride + kx] : 0.0f;
-      c = __builtin_amdgcn_mfma_f32_16x16x4f32(av, proj_s[kx * kRank + (lane & 15)], c, 0, 0, 0);
+      c2[kk & 1] = __builtin_amdgcn_mfma_f32_16x16x4f32(qbar[m * kQbarStride + kx],
+                                                        proj_s[kx * kRank + (lane & 15)], c2[kk & 1], 0, 0, 0);
     }
+    const f32x4 c = c2[0] + c2[1];
+    // row 16 t + 4 (lane / 16) + i, column j = lane % 16: the scale exponent
+    // from the row max, then each digit's nibble, OR-combined over the eight
+    // columns of a word
+    const int j = lane & 15;
+    int ex[4];
+    uint32_t w[4][kQDigits];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      (void)frexpf(max16(fabsf(c[i])), &ex[i]);
+      const uint32_t u = (uint32_t)((int)rintf(ldexpf(c[i], kQFracBits - ex[i])) + 0x888888);
+#pragma unroll
+      for (int k = 0; k < kQDigits; ++k) w[i][k] = (((u >> (4 * k)) & 15u) ^ 8u) << (4 * (j & 7));
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < kQDigits; ++k) w[i][k] |= dpp_u32<kDppXor1>(w[i][k]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < kQDigits; ++k) w[i][k] |= dpp_u32<kDppXor2>(w[i][k]);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int k = 0; k < kQDigits; ++k) w[i][k] |= dpp_u32<kDppHalfMirror>(w[i][k]);
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int row = 16 * t + 4 * (lane >> 4) + i;
-      if (row < hkv) qt_s[row * kRank + (lane & 15)] = c[i];
+      if (row < hkv && (j & 7) == 0) {
+#pragma unroll
+        for (int k = 0; k < kQDigits; ++k) qd_s[(row * kQDigits + k) * 2 + (j >> 3)] = w[i][k];
+      }
+      if (row < hkv && j == 0) qf_s[row] = ldexpf(1.0f, ex[i] - kQFracBits);
     }
   }
   __syncthreads();
@@ -258,14 +312,29 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
   for (int h0 = 0; h0 < hkv; h0 += kSalsHeads) {
     const bool hv = h0 + x < hkv;
     const int hh = hv ? h0 + x : h0;
-    float qt[kRank];
+    uint2 qd[kQDigits];
 #pragma unroll
-    for (int j = 0; j < kRank; ++j) qt[j] = qt_s[hh * kRank + j];
+    for (int k = 0; k < kQDigits; ++k) qd[k] = reinterpret_cast<const uint2*>(qd_s)[hh * kQDigits + k];
+    const float fz = tau_log2e * qf_s[hh];
     float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.0f, 0.0f};
     for (int t0 = 0; t0 < unit_tokens; t0 += 64) {
       if (h0 > 0 || t0 > 0) {  // the first pass was fetched ahead
         issue_pt(t0);
         issue_codes(hh);
+      }
+      // sum_j c_j Q_j per token, exact (|.| < 7 * 16 * 2^22): Horner over the
+      // digits, the 16 tokens interleaved
+      int dot[16];
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) dot[ii] = 0;
+#pragma unroll
+      for (int k = kQDigits - 1; k >= 0; --k) {
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          dot[ii] = __builtin_amdgcn_sdot8((int)cw[ii].x, (int)qd[k].x, dot[ii], false);
+          dot[ii] = __builtin_amdgcn_sdot8((int)cw[ii].y, (int)qd[k].y, dot[ii], false);
+          if (k > 0) dot[ii] = (int)((uint32_t)dot[ii] << 4);
+        }
       }
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
@@ -273,13 +342,8 @@ __global__ __launch_bounds__(256) void sals_score_kernel(
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int ii = 8 * blk + i;
-          float dot = 0.0f;
-#pragma unroll
-          for (int j = 0; j < kRank; ++j) {
-            const uint32_t word = j < 8 ? cw[ii].x : cw[ii].y;
-            dot = fmaf(qt[j], (float)((int)(word << (28 - 4 * (j & 7))) >> 28), dot);
-          }
-          z[i] = (ok[ii] && hv) ? tau_log2e * (f16_to_f32(sw[ii]) * dot) : -INFINITY;
+          const float zv = fz * (f16_to_f32(sw[ii]) * (float)dot[ii]);
+          z[i] = (ok[ii] && hv) ? zv : -INFINITY;
           zmax = fmaxf(zmax, z[i]);
         }
         if (zmax != -INFINITY) {
@@ -371,14 +435,25 @@ hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,
   dim3 grid((max_units + kSalsUnitsPerWG - 1) / kSalsUnitsPerWG, s.B);
   const float tl2 = tau * kLog2e;
   const size_t smem = sals_smem_bytes(s.Hkv);
-  if (q_dtype == SA_F32)
-    hipLaunchKernelGGL(sals_score_kernel<SA_F32>, grid, dim3(256), smem, st, q, s.Hq, codes, scales,
-                       proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2, scores,
-                       max_units);
-  else
-    hipLaunchKernelGGL(sals_score_kernel<SA_BF16>, grid, dim3(256), smem, st, q, s.Hq, codes, scales,
-                       proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2, scores,
-                       max_units);
+#define SA_SS(QQ, GG)                                                                            \
+  hipLaunchKernelGGL((sals_score_kernel<QQ, GG>), grid, dim3(256), smem, st, q, s.Hq, codes,     \
+                     scales, proj, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, tl2,  \
+                     scores, max_units)
+#define SA_SG(QQ)                     \
+  switch (s.Hq / s.Hkv) {             \
+    case 1: SA_SS(QQ, 1); break;      \
+    case 2: SA_SS(QQ, 2); break;      \
+    case 4: SA_SS(QQ, 4); break;      \
+    case 8: SA_SS(QQ, 8); break;      \
+    default: SA_SS(QQ, 16); break;    \
+  }
+  if (q_dtype == SA_F32) {
+    SA_SG(SA_F32)
+  } else {
+    SA_SG(SA_BF16)
+  }
+#undef SA_SG
+#undef SA_SS
   return hipGetLastError();
 }
 
