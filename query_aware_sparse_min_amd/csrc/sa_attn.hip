@@ -27,14 +27,16 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     cnt = min(num_sel[(size_t)b * hkv + h], max_sel);
   }
   const int j0 = split * pps, j1 = min(j0 + pps, cnt);
+  // the split's list entries are read together with the list length
+  const int jcap = sel ? min(j0 + pps, max_sel) : -1;
   float* part = partials + (((size_t)b * hkv + h) * nsplit + split) * G * kPartStride;
   // four or more bf16 query heads per kv-head: scores on the matrix cores
   if constexpr (G >= 4 && QT == SA_BF16 && (KT == SA_BF16 || KT == SA_I8))
     attend_range_mfma<KT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
-                             lst, j0, j1, scale_log2, part, sm);
+                             lst, j0, j1, scale_log2, part, sm, jcap);
   else
     attend_range<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
-                            lst, j0, j1, scale_log2, part, sm);
+                            lst, j0, j1, scale_log2, part, sm, nullptr, jcap);
 }
 
 // grid (G, Hkv, B), block 256: merge the splits of one query head of one list
@@ -73,14 +75,20 @@ hipError_t attn_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, cons
 }  // namespace
 
 AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len) {
-  // Enough workgroups to cover the 256 CUs several times over; at least one
-  // page per wave of a split.
-  constexpr long kTargetWGs = 2048;
+  // Selected lists: about two workgroups per CU, each wave taking the same
+  // whole number of pages.  Measured on the GQA, SALS and large workloads,
+  // fewer and longer splits beat filling the CUs: every split pays the list,
+  // page-table and query round trips once, and the merge reads one record per
+  // split.  Past 16 pages per wave the pass is bound by bandwidth, and more
+  // workgroups (about eight per CU) keep more bytes in flight.
+  constexpr long kLatencyWGs = 512, kBandwidthWGs = 2048, kMaxLatencyPPS = 64;
   AttnPlan p{};
   p.list_len = list_len < 1 ? 1 : list_len;
   const long lists = (long)B * Hkv;
   const int G = Hq / Hkv;
-  long pps = (lists * p.list_len + kTargetWGs - 1) / kTargetWGs;
+  const long pages = lists * p.list_len;
+  long pps = ((pages + kLatencyWGs - 1) / kLatencyWGs + 3) / 4 * 4;
+  if (pps > kMaxLatencyPPS) pps = (pages + kBandwidthWGs - 1) / kBandwidthWGs;
   if (pps < 4) pps = 4;
   p.pps = (int)pps;
   p.nsplit = (p.list_len + p.pps - 1) / p.pps;

@@ -90,9 +90,11 @@ struct WavePages {
   int j0, j1, np, num_pages, L, wave;
   int my_pp = -1, my_nv = 0;
 
+  // jcap >= j1 bounds the list entries that may be read before j1 is known
+  // (-1: j1), so that the list read need not wait for the list length
   __device__ __forceinline__ WavePages(const int32_t* pt_row_, const int32_t* lst_,
                                        const int32_t* rlst_, int j0_, int j1_, int L_,
-                                       int num_pages_)
+                                       int num_pages_, int jcap = -1)
       : pt_row(pt_row_), lst(lst_), rlst(rlst_), j0(j0_), j1(j1_),
         np((L_ + kPage - 1) / kPage), num_pages(num_pages_), L(L_),
         wave((int)(threadIdx.x >> 6)) {
@@ -106,7 +108,8 @@ struct WavePages {
       }
     } else {
       int p = -1;
-      if (j < j1) p = lst ? ld_x<COH>(lst + j) : j;
+      if (j < (jcap < 0 ? j1 : jcap)) p = lst ? ld_x<COH>(lst + j) : j;
+      if (j >= j1) p = -1;
       if (p >= 0 && p < np) {
         const int pp = pt_row[p];
         if (pp >= 0 && pp < num_pages) {
@@ -191,7 +194,8 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
                              const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
                              const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
                              int j1, float scale_log2, float* __restrict__ part,
-                             AttnSmem<G, NW>& sm, const int32_t* rlst = nullptr) {
+                             AttnSmem<G, NW>& sm, const int32_t* rlst = nullptr,
+                             int jcap = -1) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int hq = hkv * G;
@@ -209,7 +213,7 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
   }
 
-  const WavePages<COH, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages);
+  const WavePages<COH, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages, jcap);
 
   for (int jb = j0 + wave; jb < j1; jb += NW * PW) {
     PageRef pg[PW];
@@ -373,7 +377,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
                                                   const int32_t* __restrict__ pt_row, int L,
                                                   const int32_t* lst, int j0, int j1,
                                                   float scale_log2, float* __restrict__ part,
-                                                  AttnSmem<G, NW>& sm) {
+                                                  AttnSmem<G, NW>& sm, int jcap = -1) {
   static_assert(G >= 1 && G <= 16, "one MFMA column per query head");
   static_assert(KT == SA_BF16 || KT == SA_I8, "K enters the MFMA as bf16");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -403,7 +407,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
 
-  const WavePages<false, NW> page_of(pt_row, lst, nullptr, j0, j1, L, num_pages);
+  const WavePages<false, NW> page_of(pt_row, lst, nullptr, j0, j1, L, num_pages, jcap);
   for (int jb = j0 + wave; jb < j1; jb += NW) {
     const PageRef pg = page_of(jb);
     const size_t ppl = pg.pp >= 0 ? (size_t)pg.pp : 0;  // empty slot: load page 0, result unused

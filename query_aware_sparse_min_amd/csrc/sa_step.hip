@@ -44,7 +44,7 @@ constexpr int kStepWaves = 12;              // one workgroup per CU: 12 waves, 1
 constexpr int kStepThreads = 64 * kStepWaves;
 constexpr int kScoreIT = (64 + kStepWaves - 1) / kStepWaves;  // load pairs per lane per score pass
 constexpr int kScorePass = 4 * kStepWaves * kScoreIT;          // pages per score pass (>= 256)
-constexpr int kChunkGrain = 64;                                // chunk sizes are multiples of this
+constexpr int kChunkGrain = 16;                                // chunk sizes are multiples of this
 
 template <int G>
 union StepSmem {
