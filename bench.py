@@ -58,7 +58,8 @@ def parse():
                     help="run a few steps and a plain copy of known size, for a counter run")
     ap.add_argument("--configs", default="",
                     help="instead of the headline line, one line per listed workload "
-                         "(1-5, 5d = config 5 with every page kept), e.g. --configs 1,3,4,5,5d")
+                         "(1-5, 5d = config 5 with every page kept, 2a / 4a = the decode-time "
+                         "append on config 2 / 4), e.g. --configs 1,3,4,5,5d,2a,4a")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc outputs")
     return ap.parse_args()
@@ -122,7 +123,8 @@ def main():
         sys.exit(2)
     if args.configs:
         for name in args.configs.split(","):
-            config_line(name.strip(), args)
+            name = name.strip()
+            (append_line if name.endswith("a") else config_line)(name, args)
         return
     import numpy as np
     import torch
@@ -408,6 +410,91 @@ def config_line(name, args):
     }
     print(json.dumps(rec), flush=True)
     del copies, d, ws, dws
+    torch.cuda.empty_cache()
+
+
+def append_line(name, args):
+    """The decode-time append (sa_append_kv) on a workload's full-size cache: one
+    token per sequence written into its page plus the incremental metadata
+    update, timed as a HIP graph of K appends.  The appended token is each
+    sequence's current last token again, which leaves cache and metadata
+    unchanged (the max/min fold and the index key are idempotent), so every
+    replay does the same work.  Algorithmic bytes: the new K/V rows read and
+    written (int8: and their scales), plus the page metadata read and written
+    (Quest: the page's max and min rows) or written (SALS: codes and scale)."""
+    import numpy as np
+    import torch
+
+    import query_aware_sparse_min_amd as sa
+    import synth
+
+    if not os.path.exists(sa.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    sa.load()
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    print(f"[bench] append on config {name[0]}: generating inputs", file=sys.stderr, flush=True)
+    wl = synth.make_config(int(name[0]))
+    d = synth.to_device(wl, dev)
+    seqs = sa.Seqs(d.page_table, d.seq_lens)
+    mode = sa.SA_MODE_QUEST if wl.mode == "quest" else sa.SA_MODE_SALS
+    cfg = sa.SelectCfg(mode, wl.unit_tokens, wl.k_compete, wl.n_head_forced, wl.n_tail_forced,
+                       wl.rank, d.proj, wl.lse_scale)
+    kv = sa.KVCache(d.k, d.v, d.k_scale, d.v_scale)
+    meta, mscale = sa.alloc_meta(kv, cfg)
+    sa.sa_build_page_meta(kv, seqs, cfg, meta, mscale)
+    t = wl.seq_lens.astype(np.int64) - 1
+    pp = torch.from_numpy(wl.page_table[np.arange(wl.B), t // 16].astype(np.int64)).to(dev)
+    sl = torch.from_numpy((t % 16).astype(np.int64)).to(dev)
+    new = {n: getattr(d, n)[pp, sl].contiguous() for n in ("k", "v", "k_scale", "v_scale")
+           if getattr(d, n) is not None}
+
+    def append(i):
+        sa.sa_append_kv(new["k"], new["v"], kv, seqs, cfg, meta, mscale, new.get("k_scale"),
+                        new.get("v_scale"))
+
+    stream = torch.cuda.current_stream()
+    K = max(10, min(args.steps, 200))
+    for i in range(5):
+        append(i)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    cap = torch.cuda.Stream()
+    cap.wait_stream(stream)
+    with torch.cuda.stream(cap):
+        with torch.cuda.graph(g, stream=cap):
+            for i in range(K):
+                append(i)
+    stream.wait_stream(cap)
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record(stream)
+    g.replay()
+    b.record(stream)
+    torch.cuda.synchronize()
+    us = a.elapsed_time(b) / K * 1e3
+    es = {"f32": 4, "bf16": 2, "i8": 1}[wl.kv_dtype]
+    row = wl.B * wl.Hkv * wl.d * es
+    nbytes = 2 * 2 * row  # K and V rows: read from the new-token buffers, written into the cache
+    if wl.kv_dtype == "i8":
+        nbytes += 2 * 2 * wl.B * wl.Hkv * 2
+    if wl.mode == "quest":
+        nbytes += 2 * 2 * row  # the page's max and min rows, read and written
+    else:
+        nbytes += wl.B * wl.Hkv * (wl.rank // 2 + 2)  # codes and scale of the token
+    rec = {
+        "metric": f"decode-time append µs + effective HBM GB/s, {wl.name}",
+        "workload": wl.name + "-append", "batch": wl.B, "num_kv_heads": wl.Hkv,
+        "kv_dtype": wl.kv_dtype,
+        "metadata": "quest min/max fold" if wl.mode == "quest" else "sals int4 index key",
+        "append_us": round(us, 2), "append_bytes": int(nbytes),
+        "gbs": round(nbytes / (us * 1e-6) / 1e9, 1), "steps": K,
+        "timing": "HIP graph of K appends, replayed once between two events",
+    }
+    print(json.dumps(rec), flush=True)
+    del d, kv, meta, mscale, new
     torch.cuda.empty_cache()
 
 

@@ -145,6 +145,34 @@ size_t sa_meta_scale_bytes(const sa_kv_cache *kv, const sa_select_cfg *cfg);
 int sa_build_page_meta(const sa_kv_cache *kv, const sa_seqs *seqs, const sa_select_cfg *cfg,
                        void *meta, uint16_t *meta_scale, void *stream);
 
+/*
+ * sa_append_kv - decode-time insert of one new token per sequence with the
+ * incremental metadata update [Quest, insert-time update M <- max(M, k),
+ * m <- min(m, k) when a token joins a page; SALS, per-token low-rank
+ * preprocessing of the index key].  For every b the new token is position
+ * t = seq_lens[b] - 1 (seq_lens already counts it): slot s = t mod 16 of
+ * physical page pp = page_table[b, t / 16].
+ *  - k_new, v_new: [batch, num_kv_heads, head_dim] in the cache dtype (SA_I8:
+ *    codes, with k_scale_new, v_scale_new = [batch, num_kv_heads] fp16 bits;
+ *    both NULL for other dtypes).  They are copied into slot s of page pp of
+ *    kv->k, kv->v (and kv->k_scale, kv->v_scale): this call WRITES the cache
+ *    buffers that sa_kv_cache names (declared const for the read-only calls).
+ *  - QUEST: s == 0 starts the page, M = m = k; otherwise M <- max(M, k) and
+ *    m <- min(m, k) per (kv-head, dim), with the ordered comparisons that
+ *    sa_build_page_meta folds a page with.  After any run of appends, meta
+ *    equals a rebuild over the updated cache, bit for bit.
+ *  - SALS: the token's codes and scale, exactly as sa_build_page_meta
+ *    computes them (meta_scale required).
+ * A sequence whose seq_lens[b] is outside [1, max_pages * 16], or whose page
+ * id is outside [0, num_pages), is skipped (not reported).  The tokens of one
+ * call belong to distinct pages (a page belongs to one sequence), so a call
+ * has no write conflicts.  Not available for QUEST with SA_I8 caches
+ * (SA_ERR_UNSUPPORTED).
+ */
+int sa_append_kv(const void *k_new, const void *v_new, const uint16_t *k_scale_new,
+                 const uint16_t *v_scale_new, const sa_kv_cache *kv, const sa_seqs *seqs,
+                 const sa_select_cfg *cfg, void *meta, uint16_t *meta_scale, void *stream);
+
 /* Units per scores row: QUEST max_pages; SALS ceil(max_pages * 16 / unit_tokens). 0 on bad input. */
 int32_t sa_max_units(const sa_seqs *seqs, const sa_select_cfg *cfg);
 

@@ -56,7 +56,7 @@ class sa_select_cfg(ctypes.Structure):
 
 
 EXPORTS = ["sa_version", "sa_status_string", "sa_meta_bytes", "sa_meta_scale_bytes",
-           "sa_build_page_meta", "sa_max_units", "sa_score_pages", "sa_max_selected",
+           "sa_build_page_meta", "sa_append_kv", "sa_max_units", "sa_score_pages", "sa_max_selected",
            "sa_topk_pages", "sa_attn_workspace_size", "sa_sparse_decode_attn",
            "sa_decode_step_workspace_size", "sa_decode_step"]
 
@@ -77,6 +77,7 @@ def load(path: str = LIB_PATH):
         "sa_meta_bytes": (SZ, [KV, CF]),
         "sa_meta_scale_bytes": (SZ, [KV, CF]),
         "sa_build_page_meta": (ctypes.c_int, [KV, SQ, CF, VP, VP, VP]),
+        "sa_append_kv": (ctypes.c_int, [VP, VP, VP, VP, KV, SQ, CF, VP, VP, VP]),
         "sa_max_units": (I32, [SQ, CF]),
         "sa_score_pages": (ctypes.c_int, [VP, I32, I32, KV, SQ, CF, VP, VP, VP, VP]),
         "sa_max_selected": (I32, [SQ, CF]),
@@ -221,6 +222,17 @@ def sa_build_page_meta(kv: KVCache, seqs: Seqs, cfg: SelectCfg, meta: torch.Tens
     _check(load().sa_build_page_meta(ctypes.byref(kv.struct()), ctypes.byref(seqs.struct()),
                                      ctypes.byref(cfg.struct()), _ptr(meta), _ptr(meta_scale),
                                      _stream(stream)), "sa_build_page_meta")
+
+
+def sa_append_kv(k_new: torch.Tensor, v_new: torch.Tensor, kv: KVCache, seqs: Seqs, cfg: SelectCfg,
+                 meta: torch.Tensor, meta_scale: Optional[torch.Tensor] = None,
+                 k_scale_new: Optional[torch.Tensor] = None, v_scale_new: Optional[torch.Tensor] = None,
+                 stream=None) -> None:
+    """Writes one new token per sequence (at seq_lens[b] - 1) into kv and updates meta."""
+    _check(load().sa_append_kv(_ptr(k_new), _ptr(v_new), _ptr(k_scale_new), _ptr(v_scale_new),
+                               ctypes.byref(kv.struct()), ctypes.byref(seqs.struct()),
+                               ctypes.byref(cfg.struct()), _ptr(meta), _ptr(meta_scale),
+                               _stream(stream)), "sa_append_kv")
 
 
 def sa_score_pages(q: torch.Tensor, kv: KVCache, seqs: Seqs, cfg: SelectCfg, meta: torch.Tensor,

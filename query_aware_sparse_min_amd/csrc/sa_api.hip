@@ -225,6 +225,26 @@ int sa_build_page_meta(const sa_kv_cache* kv, const sa_seqs* seqs, const sa_sele
                                       meta_scale, st));
 }
 
+int sa_append_kv(const void* k_new, const void* v_new, const uint16_t* k_scale_new,
+                 const uint16_t* v_scale_new, const sa_kv_cache* kv, const sa_seqs* seqs,
+                 const sa_select_cfg* cfg, void* meta, uint16_t* meta_scale, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs)) || (rc = check_cfg(cfg))) return rc;
+  if ((rc = check_mode_kv(cfg, kv))) return rc;
+  if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return SA_ERR_INVALID_ARG;
+  if (kv->dtype == SA_I8 && (!k_scale_new || !v_scale_new)) return SA_ERR_INVALID_ARG;
+  if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
+  if (cfg->mode == SA_MODE_SALS && !meta_scale) return SA_ERR_INVALID_ARG;
+  const Shapes s = shapes_of(kv->num_kv_heads, kv, seqs);
+  // the cache buffers are written: the struct's pointers are const for the
+  // read-only entry points only
+  return hip_status(launch_append(kv->dtype, cfg->mode, k_new, v_new, k_scale_new, v_scale_new,
+                                  const_cast<void*>(kv->k), const_cast<void*>(kv->v),
+                                  const_cast<uint16_t*>(kv->k_scale), const_cast<uint16_t*>(kv->v_scale),
+                                  s, seqs->page_table, seqs->seq_lens, cfg->proj, meta, meta_scale,
+                                  static_cast<hipStream_t>(stream)));
+}
+
 int sa_score_pages(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache* kv,
                    const sa_seqs* seqs, const sa_select_cfg* cfg, const void* meta,
                    const uint16_t* meta_scale, float* scores, void* stream) {

@@ -185,6 +185,11 @@ hipError_t launch_quest_meta(int dtype, const void* k, const Shapes& s, const in
 hipError_t launch_sals_index(int dtype, const void* k, const uint16_t* k_scale, const Shapes& s,
                              const int32_t* pt, const int32_t* lens, const float* proj,
                              uint8_t* codes, uint16_t* scales, hipStream_t st);
+hipError_t launch_append(int dtype, int mode, const void* k_new, const void* v_new,
+                         const uint16_t* ks_new, const uint16_t* vs_new, void* k, void* v,
+                         uint16_t* k_scale, uint16_t* v_scale, const Shapes& s, const int32_t* pt,
+                         const int32_t* lens, const float* proj, void* meta, uint16_t* meta_scale,
+                         hipStream_t st);
 hipError_t launch_quest_score(int kv_dtype, int q_dtype, const void* q, const void* meta,
                               const Shapes& s, const int32_t* pt, const int32_t* lens,
                               float* scores, hipStream_t st);

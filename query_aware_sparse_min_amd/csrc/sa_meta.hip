@@ -11,6 +11,10 @@
 //    and the int4 index key of QSI): one thread per (token, kv-head) runs the
 //    16 fp32 fused-multiply-add chains k * P in dimension order, so its codes
 //    are bit-identical to any other evaluation of the same definition.
+//  * Decode-time append of one token per sequence: the token's K/V rows into
+//    its page, then the same per-token metadata step (Quest: one more fold of
+//    M <- max(M, k), m <- min(m, k); SALS: the token's index key), so the
+//    metadata after any run of appends equals a full rebuild.
 #pragma clang fp contract(off)
 
 #include "sa_internal.h"
@@ -95,6 +99,41 @@ __global__ __launch_bounds__(256) void quest_meta_kernel(const void* __restrict_
   }
 }
 
+// Index key of one (token, kv-head) row: key elements at k + e0 .. + d - 1
+// (int8: codes times sc), P in LDS; writes the two code words and the scale.
+template <int DT>
+__device__ __forceinline__ void sals_key(const void* __restrict__ k, size_t e0, float sc,
+                                         const float* P, uint2* crow, uint16_t* srow) {
+  float acc[kRank];
+#pragma unroll
+  for (int j = 0; j < kRank; ++j) acc[j] = 0.0f;
+  for (int i = 0; i < kHeadDim; i += 8) {
+    float x[8];
+    load8<DT>(k, e0 + i, x);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const float kh = (DT == SA_I8) ? x[e] * sc : x[e];  // int8: code * scale, exact in fp32
+#pragma unroll
+      for (int j = 0; j < kRank; ++j) acc[j] = __builtin_fmaf(kh, P[(i + e) * kRank + j], acc[j]);
+    }
+  }
+  float amax = 0.0f;
+#pragma unroll
+  for (int j = 0; j < kRank; ++j) amax = fmaxf(amax, fabsf(acc[j]));
+  const _Float16 sh = (_Float16)(amax / 7.0f);  // IEEE division, then RNE to fp16
+  const float sf = (float)sh;
+  uint32_t w[2] = {0u, 0u};
+#pragma unroll
+  for (int j = 0; j < kRank; ++j) {
+    float c = 0.0f;
+    if (sf != 0.0f) c = fminf(fmaxf(__builtin_rintf(acc[j] / sf), -7.0f), 7.0f);
+    const uint32_t nib = (uint32_t)((int)c) & 0xFu;
+    w[j / 8] |= nib << (4 * (j % 8));
+  }
+  *crow = make_uint2(w[0], w[1]);
+  *srow = __builtin_bit_cast(uint16_t, sh);
+}
+
 // grid (max_pages, B), block 256; P staged in LDS (8 KiB)
 template <int DT>
 __global__ __launch_bounds__(256) void sals_index_kernel(
@@ -121,34 +160,98 @@ __global__ __launch_bounds__(256) void sals_index_kernel(
     }
     float sc = 1.0f;
     if constexpr (DT == SA_I8) sc = f16_to_f32(k_scale[row]);
-    float acc[kRank];
+    sals_key<DT>(k, row * kHeadDim, sc, P, crow, scales + row);
+  }
+}
+
+// grid (B), block 256: one new token per sequence, at t = lens[b] - 1.  Its
+// K/V rows (and int8 scales) are copied into slot t % 16 of its page, then
+// the page's metadata takes the token: QUEST folds it into (M, m) with the
+// comparisons quest_meta_kernel folds with (slot 0 starts the page); SALS
+// writes the token's index key, computed as sals_key does.
+template <int DT, bool SALS>
+__global__ __launch_bounds__(256) void append_kernel(
+    const void* __restrict__ k_new, const void* __restrict__ v_new,
+    const uint16_t* __restrict__ ks_new, const uint16_t* __restrict__ vs_new, void* k_, void* v_,
+    uint16_t* k_scale, uint16_t* v_scale, int num_pages, int hkv, const int32_t* __restrict__ pt,
+    const int32_t* __restrict__ lens, int max_pages, const float* __restrict__ proj, void* meta_,
+    uint16_t* meta_scale) {
+  constexpr int ES = DT == SA_F32 ? 4 : DT == SA_BF16 ? 2 : 1;  // element bytes
+  __shared__ float P[SALS ? kHeadDim * kRank : 1];
+  const int b = blockIdx.x;
+  const int L = lens[b];
+  if (L < 1 || L > max_pages * kPage) return;
+  const int t = L - 1, slot = t % kPage;
+  const int pp = pt[(size_t)b * max_pages + t / kPage];
+  if (pp < 0 || pp >= num_pages) return;
+  const int row = hkv * kHeadDim;  // elements per token row
+  const size_t src = (size_t)b * row, dst = ((size_t)pp * kPage + slot) * row;
+  // K / V rows, 16 bytes per thread and step
+  const int row16 = row * ES / 16;
+  for (int c = threadIdx.x; c < row16; c += blockDim.x) {
+    reinterpret_cast<uint4*>(static_cast<char*>(k_) + dst * ES)[c] =
+        reinterpret_cast<const uint4*>(static_cast<const char*>(k_new) + src * ES)[c];
+    reinterpret_cast<uint4*>(static_cast<char*>(v_) + dst * ES)[c] =
+        reinterpret_cast<const uint4*>(static_cast<const char*>(v_new) + src * ES)[c];
+  }
+  if constexpr (DT == SA_I8) {
+    for (int h = threadIdx.x; h < hkv; h += blockDim.x) {
+      k_scale[((size_t)pp * kPage + slot) * hkv + h] = ks_new[(size_t)b * hkv + h];
+      v_scale[((size_t)pp * kPage + slot) * hkv + h] = vs_new[(size_t)b * hkv + h];
+    }
+  }
+  if constexpr (SALS) {
+    for (int i = threadIdx.x; i < kHeadDim * kRank; i += blockDim.x) P[i] = proj[i];
+    __syncthreads();
+    // one 16-lane row per kv-head, lane j running output j's chain: the same
+    // fmaf order, maximum, scale and codes as sals_key, sixteen chains wide
+    const int j = threadIdx.x & 15;
+    for (int h = threadIdx.x >> 4; h < hkv; h += blockDim.x >> 4) {
+      const float sc = DT == SA_I8 ? f16_to_f32(ks_new[(size_t)b * hkv + h]) : 1.0f;
+      float acc = 0.0f;
+      for (int i = 0; i < kHeadDim; i += 8) {
+        float x[8];
+        load8<DT>(k_new, src + (size_t)h * kHeadDim + i, x);
 #pragma unroll
-    for (int j = 0; j < kRank; ++j) acc[j] = 0.0f;
-    for (int i = 0; i < kHeadDim; i += 8) {
-      float x[8];
-      load8<DT>(k, row * kHeadDim + i, x);
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float kh = (DT == SA_I8) ? x[e] * sc : x[e];  // int8: code * scale, exact in fp32
-#pragma unroll
-        for (int j = 0; j < kRank; ++j) acc[j] = __builtin_fmaf(kh, P[(i + e) * kRank + j], acc[j]);
+        for (int e = 0; e < 8; ++e) {
+          const float kh = (DT == SA_I8) ? x[e] * sc : x[e];
+          acc = __builtin_fmaf(kh, P[(i + e) * kRank + j], acc);
+        }
       }
+      const float amax = max16(fabsf(acc));
+      const _Float16 sh = (_Float16)(amax / 7.0f);  // IEEE division, then RNE to fp16
+      const float sf = (float)sh;
+      const float c = sf != 0.0f ? fminf(fmaxf(__builtin_rintf(acc / sf), -7.0f), 7.0f) : 0.0f;
+      uint32_t w = ((uint32_t)((int)c) & 0xFu) << (4 * (j & 7));
+      w |= dpp_u32<kDppXor1>(w);
+      w |= dpp_u32<kDppXor2>(w);
+      w |= dpp_u32<kDppHalfMirror>(w);
+      const size_t r = ((size_t)pp * kPage + slot) * hkv + h;
+      if ((j & 7) == 0) reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(meta_) + r * (kRank / 2))[j >> 3] = w;
+      if (j == 0) meta_scale[r] = __builtin_bit_cast(uint16_t, sh);
     }
-    float amax = 0.0f;
+  } else if constexpr (DT != SA_I8) {
+    char* meta = static_cast<char*>(meta_);
+    for (int c = threadIdx.x; c < row / 8; c += blockDim.x) {
+      const int h = c / (kHeadDim / 8), i0 = (c % (kHeadDim / 8)) * 8;
+      Chunk8<DT> x;
+      x.load(static_cast<const char*>(k_new) + (src + (size_t)c * 8) * ES);
+      char* mxp = meta + ((((size_t)h * num_pages + pp) * 2 + 0) * kHeadDim + i0) * ES;
+      char* mnp = meta + ((((size_t)h * num_pages + pp) * 2 + 1) * kHeadDim + i0) * ES;
+      Chunk8<DT> mx = x, mn = x;
+      if (slot > 0) {
+        mx.load(mxp);
+        mn.load(mnp);
 #pragma unroll
-    for (int j = 0; j < kRank; ++j) amax = fmaxf(amax, fabsf(acc[j]));
-    const _Float16 sh = (_Float16)(amax / 7.0f);  // IEEE division, then RNE to fp16
-    const float sf = (float)sh;
-    uint32_t w[2] = {0u, 0u};
-#pragma unroll
-    for (int j = 0; j < kRank; ++j) {
-      float c = 0.0f;
-      if (sf != 0.0f) c = fminf(fmaxf(__builtin_rintf(acc[j] / sf), -7.0f), 7.0f);
-      const uint32_t nib = (uint32_t)((int)c) & 0xFu;
-      w[j / 8] |= nib << (4 * (j % 8));
+        for (int e = 0; e < 8; ++e) {
+          const float xv = x.val(e);
+          if (xv > mx.val(e)) mx.set(e, x.bits(e));
+          if (xv < mn.val(e)) mn.set(e, x.bits(e));
+        }
+      }
+      mx.store(mxp);
+      mn.store(mnp);
     }
-    *crow = make_uint2(w[0], w[1]);
-    scales[row] = __builtin_bit_cast(uint16_t, sh);
   }
 }
 
@@ -183,6 +286,30 @@ hipError_t launch_sals_index(int dtype, const void* k, const uint16_t* k_scale, 
       hipLaunchKernelGGL(sals_index_kernel<SA_I8>, grid, dim3(256), 0, st, k, k_scale,
                          s.num_pages, s.Hkv, pt, lens, s.max_pages, proj, codes, scales);
   }
+  return hipGetLastError();
+}
+
+hipError_t launch_append(int dtype, int mode, const void* k_new, const void* v_new,
+                         const uint16_t* ks_new, const uint16_t* vs_new, void* k, void* v,
+                         uint16_t* k_scale, uint16_t* v_scale, const Shapes& s, const int32_t* pt,
+                         const int32_t* lens, const float* proj, void* meta, uint16_t* meta_scale,
+                         hipStream_t st) {
+#define SA_AP(DT, SALS)                                                                          \
+  hipLaunchKernelGGL((append_kernel<DT, SALS>), dim3(s.B), dim3(256), 0, st, k_new, v_new, ks_new, \
+                     vs_new, k, v, k_scale, v_scale, s.num_pages, s.Hkv, pt, lens, s.max_pages,   \
+                     proj, meta, meta_scale)
+  const bool sals = mode == SA_MODE_SALS;
+  switch (dtype) {
+    case SA_F32:
+      if (sals) SA_AP(SA_F32, true); else SA_AP(SA_F32, false);
+      break;
+    case SA_BF16:
+      if (sals) SA_AP(SA_BF16, true); else SA_AP(SA_BF16, false);
+      break;
+    default:
+      SA_AP(SA_I8, true);  // QUEST metadata is not kept for int8 caches
+  }
+#undef SA_AP
   return hipGetLastError();
 }
 

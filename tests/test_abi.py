@@ -175,3 +175,23 @@ def test_topk_and_meta_argument_checks():
     assert lib.sa_build_page_meta(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(sals), FAKE, None, None) == sa.SA_ERR_INVALID_ARG
     kv3 = _kv(num_kv_heads=3)
     assert lib.sa_build_page_meta(ctypes.byref(kv3), ctypes.byref(seqs), ctypes.byref(sals), FAKE, FAKE, None) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_append_argument_checks():
+    lib = _lib()
+    seqs = _seqs()
+    sals = _cfg(mode=sa.SA_MODE_SALS, unit_tokens=64, k_compete=32, n_head_forced=0, n_tail_forced=2,
+                proj=FAKE)
+
+    def call(kv, cfg, k_new=FAKE, v_new=FAKE, ks=None, vs=None, meta=FAKE, mscale=None):
+        return lib.sa_append_kv(k_new, v_new, ks, vs, ctypes.byref(kv), ctypes.byref(seqs),
+                                ctypes.byref(cfg), meta, mscale, None)
+
+    assert call(_kv(), _cfg(), k_new=None) == sa.SA_ERR_INVALID_ARG
+    assert call(_kv(), _cfg(), v_new=FAKE + 8) == sa.SA_ERR_INVALID_ARG       # 16-byte alignment
+    assert call(_kv(), _cfg(), meta=None) == sa.SA_ERR_INVALID_ARG
+    i8 = _kv(dtype=sa.SA_I8, k_scale=FAKE, v_scale=FAKE)
+    assert call(i8, _cfg(), ks=FAKE, vs=FAKE) == sa.SA_ERR_UNSUPPORTED       # no Quest metadata for int8
+    assert call(i8, sals, mscale=FAKE) == sa.SA_ERR_INVALID_ARG              # int8 rows need their scales
+    assert call(_kv(), sals) == sa.SA_ERR_INVALID_ARG                        # SALS needs meta_scale
+    assert call(_kv(num_kv_heads=3), sals, mscale=FAKE) == sa.SA_ERR_UNSUPPORTED
