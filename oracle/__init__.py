@@ -60,6 +60,8 @@ def _load():
     lib.oracle_sals_scores_float.restype = None
     lib.oracle_select.argtypes = [vp, i, i, i, vp, i, i, i, i, i, i, vp, vp]
     lib.oracle_select.restype = i
+    lib.oracle_probe_scores.argtypes = [vp, i, i, vp, i, vp, i, i, i, vp, vp, i, i, i, i, vp, vp]
+    lib.oracle_probe_scores.restype = None
     lib.oracle_attention.argtypes = [vp, i, i, vp, vp, i, vp, vp, i, i, i, vp, vp, i, i, vp, vp, i,
                                      d, vp, i, vp]
     lib.oracle_attention.restype = None
@@ -161,6 +163,25 @@ def sals_scores_float(q: np.ndarray, q_dtype: str, keys_lr: np.ndarray, proj: np
     return sc
 
 
+def probe_scores(q: np.ndarray, q_dtype: str, k: np.ndarray, kv_dtype: str,
+                 k_scale: Optional[np.ndarray], page_table: np.ndarray, seq_lens: np.ndarray,
+                 unit_tokens: int, n_probe: int) -> Tuple[np.ndarray, np.ndarray]:
+    """Probe-sampling block scores: max over evenly probed tokens and the group's heads of
+    q_g . k_t, plus the absolute magnitude; blocks past the sequence get -inf."""
+    q, k = _c(q), _c(k)
+    B, Hq, d = q.shape
+    P, S, Hkv, _ = k.shape
+    pt, sl = _c(page_table, np.int32), _c(seq_lens, np.int32)
+    mp = pt.shape[1]
+    mu = -(-mp * PAGE // unit_tokens)
+    sc = np.empty((B, Hkv, mu), dtype=np.float64)
+    ab = np.empty((B, Hkv, mu), dtype=np.float64)
+    _load().oracle_probe_scores(_p(q), DTYPES[q_dtype], Hq, _p(k), DTYPES[kv_dtype],
+                                _p(_c(k_scale, np.uint16)), Hkv, S, d, _p(pt), _p(sl), B, mp,
+                                unit_tokens, n_probe, _p(sc), _p(ab))
+    return sc, ab
+
+
 def select(scores: np.ndarray, seq_lens: np.ndarray, unit_tokens: int, k: int, n_head: int,
            n_tail: int, max_sel: int) -> Tuple[np.ndarray, np.ndarray]:
     """Exact top-k of the middle units + forced head/tail units, as ascending page lists."""
@@ -203,7 +224,9 @@ def attention(q: np.ndarray, q_dtype: str, k: np.ndarray, v: np.ndarray, kv_dtyp
 # composed decode step (scores -> selection -> attention)
 # ----------------------------------------------------------------------------
 def build_meta(wl) -> Tuple[np.ndarray, Optional[np.ndarray]]:
-    """Quest: (meta, None); SALS: (codes, scales)."""
+    """Quest: (meta, None); SALS: (codes, scales); probe sampling: (None, None), it reads K."""
+    if wl.mode == "probe":
+        return None, None
     if wl.mode == "quest":
         return quest_meta(wl.k, wl.kv_dtype, wl.page_table, wl.seq_lens), None
     return sals_index(wl.k, wl.kv_dtype, wl.k_scale, wl.page_table, wl.seq_lens, wl.proj)
@@ -211,6 +234,9 @@ def build_meta(wl) -> Tuple[np.ndarray, Optional[np.ndarray]]:
 
 def score(wl, meta, meta_scale, q=None) -> Tuple[np.ndarray, np.ndarray]:
     q = wl.q if q is None else q
+    if wl.mode == "probe":
+        return probe_scores(q, wl.q_dtype, wl.k, wl.kv_dtype, wl.k_scale, wl.page_table,
+                            wl.seq_lens, wl.unit_tokens, wl.n_probe)
     if wl.mode == "quest":
         return quest_scores(q, wl.q_dtype, meta, wl.kv_dtype, wl.page_table, wl.seq_lens)
     return sals_scores(q, wl.q_dtype, meta, meta_scale, wl.proj, wl.page_table, wl.seq_lens, wl.Hkv,

@@ -26,6 +26,8 @@
  *           selected set only.
  *  [SeqO1]  "SequenceO1" explainer (mhpn.cn): sketch attention and the
  *           two-kernel boundary; retention 100% must reproduce full attention.
+ *  [RK] also: the probe signal (keys sampled evenly inside a block, the
+ *           largest dot product with the query as the block's score).
  *
  * Layouts (row-major):
  *   q        [B, Hq, d]              fp32 or bf16 bits
@@ -516,6 +518,62 @@ void oracle_attention(const void *q, int q_dtype, int hq, const void *k, const v
   free(tok);
   free(acc);
   free(qrow);
+}
+
+/* ------------------------------------------------- probe-sampling scores
+ * [RK] §1-§2 (the probe signal of the block selector): a block's potential
+ * attention score is the largest dot product of the query with a few keys
+ * taken evenly inside the block, so a needle in the middle of an otherwise
+ * dull block is not missed, at a cost of n_probe rows per block.
+ * Block u of sequence b covers positions [u*U, min((u+1)*U, L)); with len its
+ * token count and step = max(1, len / n_probe) (integer division), the probed
+ * positions are u*U, u*U + step, u*U + 2*step, ... below the block end.
+ * score = max over the probed tokens t and over the group's query heads g of
+ * q_g . k_t (unscaled; GQA groups share one selection, as for Quest).  Blocks
+ * past the sequence get -inf.  abs_scale = max over the same (t, g) of
+ * sum_i |q_gi k_ti| (the magnitude the fp32 sums are judged against).
+ */
+void oracle_probe_scores(const void *q, int q_dtype, int hq, const void *k, int dtype,
+                         const uint16_t *k_scale, int hkv, int S, int d, const int32_t *page_table,
+                         const int32_t *seq_lens, int B, int max_pages, int unit_tokens, int n_probe,
+                         double *scores, double *abs_scale) {
+  int G = hq / hkv;
+  int max_units = ceil_div(max_pages * S, unit_tokens);
+  for (int b = 0; b < B; ++b) {
+    int L = seq_lens[b];
+    int nu = ceil_div(L, unit_tokens);
+    for (int h = 0; h < hkv; ++h) {
+      for (int u = 0; u < max_units; ++u) {
+        size_t o = ((size_t)b * hkv + h) * max_units + u;
+        if (u >= nu) {
+          scores[o] = -INFINITY;
+          if (abs_scale) abs_scale[o] = 0.0;
+          continue;
+        }
+        int t0 = u * unit_tokens, t1 = t0 + unit_tokens < L ? t0 + unit_tokens : L;
+        int step = (t1 - t0) / n_probe;
+        if (step < 1) step = 1;
+        double best = -INFINITY, amax = 0.0;
+        for (int t = t0; t < t1; t += step) {
+          int pp = page_table[(size_t)b * max_pages + t / S];
+          size_t row = ((size_t)pp * S + (t % S)) * hkv + h;
+          for (int g = 0; g < G; ++g) {
+            double dot = 0.0, a = 0.0;
+            for (int i = 0; i < d; ++i) {
+              double x = q_value(q, q_dtype, ((size_t)b * hq + (size_t)h * G + g) * d + i) *
+                         kv_value(k, dtype, row * d + i, k_scale, row);
+              dot += x;
+              a += fabs(x);
+            }
+            if (dot > best) best = dot;
+            if (a > amax) amax = a;
+          }
+        }
+        scores[o] = best;
+        if (abs_scale) abs_scale[o] = amax;
+      }
+    }
+  }
 }
 
 int oracle_abi_version(void) { return 1; }

@@ -167,7 +167,7 @@ class Workload:
     v_scale: Optional[np.ndarray]
     page_table: np.ndarray  # int32 [B, max_pages]; -1 past each sequence's pages
     seq_lens: np.ndarray    # int32 [B]
-    mode: str               # 'quest' | 'sals'
+    mode: str               # 'quest' | 'sals' | 'probe'
     unit_tokens: int
     k_compete: int
     n_head_forced: int
@@ -178,6 +178,7 @@ class Workload:
     softmax_scale: float = 0.0
     seed: int = 0
     needles: List[Tuple[int, int, int, int]] = field(default_factory=list)  # (b, kv_head, page, slot)
+    n_probe: int = 8        # probe sampling: keys probed per block
 
     @property
     def num_pages(self) -> int:
@@ -272,7 +273,8 @@ def make_custom(B: int = 1, Hq: int = 8, Hkv: int = 8, lens=(2048,), kv_dtype: s
                 n_tail_forced: Optional[int] = None, unit_tokens: Optional[int] = None,
                 page_table: str = "contiguous", seed: int = 7, max_pages: Optional[int] = None,
                 kv_chan_scale: Optional[np.ndarray] = None, q_chan_scale: Optional[np.ndarray] = None,
-                rank: int = 16, extra_pages: int = 0, name: str = "custom") -> Workload:
+                rank: int = 16, extra_pages: int = 0, name: str = "custom",
+                n_probe: int = 8) -> Workload:
     """Seeded workload of arbitrary shape (used for parity cases and config builders).
 
     kv_dtype 'i8' draws fp32 N(0,1) keys/values and quantises each
@@ -305,6 +307,13 @@ def make_custom(B: int = 1, Hq: int = 8, Hkv: int = 8, lens=(2048,), kv_dtype: s
         if k_compete is None:
             k_compete = (budget_pages if budget_pages is not None else 16) - fh - ft
         proj = None
+    elif mode == "probe":
+        ut = unit_tokens or 32
+        fh = 0 if n_head_forced is None else n_head_forced
+        ft = 1 if n_tail_forced is None else n_tail_forced
+        if k_compete is None:
+            k_compete = (budget_pages * PAGE // ut if budget_pages is not None else 32) - fh - ft
+        proj = None
     else:
         ut = unit_tokens or 64
         fh = 0 if n_head_forced is None else n_head_forced
@@ -316,7 +325,7 @@ def make_custom(B: int = 1, Hq: int = 8, Hkv: int = 8, lens=(2048,), kv_dtype: s
                     k=k, v=v, k_scale=ks, v_scale=vs, page_table=pt, seq_lens=lens, mode=mode,
                     unit_tokens=ut, k_compete=int(k_compete), n_head_forced=fh, n_tail_forced=ft,
                     proj=proj, rank=rank, lse_scale=1.0 / math.sqrt(d),
-                    softmax_scale=1.0 / math.sqrt(d), seed=seed)
+                    softmax_scale=1.0 / math.sqrt(d), seed=seed, n_probe=n_probe)
 
 
 CONFIG_NAMES = {
