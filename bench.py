@@ -58,8 +58,9 @@ def parse():
                     help="run a few steps and a plain copy of known size, for a counter run")
     ap.add_argument("--configs", default="",
                     help="instead of the headline line, one line per listed workload "
-                         "(1-5, 5d = config 5 with every page kept, 2a / 4a = the decode-time "
-                         "append on config 2 / 4), e.g. --configs 1,3,4,5,5d,2a,4a")
+                         "(1-5, 5d = config 5 with every page kept, 2p = config 2 selected by "
+                         "probe sampling, 2a / 4a = the decode-time append on config 2 / 4), "
+                         "e.g. --configs 1,3,4,5,5d,2p,2a,4a")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc outputs")
     return ap.parse_args()
@@ -328,14 +329,14 @@ def config_line(name, args):
     torch.cuda.set_device(dev)
     t0 = time.time()
     print(f"[bench] config {name}: generating inputs", file=sys.stderr, flush=True)
-    wl = synth.make_config(int(name[0]), dense=name.endswith("d"))
+    wl = synth.make_config(int(name[0]), dense=name.endswith("d"), probe="p" in name[1:])
     d = synth.to_device(wl, dev)
     print(f"[bench] config {name}: inputs on the GPU after {time.time() - t0:.0f} s", file=sys.stderr,
           flush=True)
     seqs = sa.Seqs(d.page_table, d.seq_lens)
-    mode = sa.SA_MODE_QUEST if wl.mode == "quest" else sa.SA_MODE_SALS
+    mode = {"quest": sa.SA_MODE_QUEST, "sals": sa.SA_MODE_SALS, "probe": sa.SA_MODE_PROBE}[wl.mode]
     cfg = sa.SelectCfg(mode, wl.unit_tokens, wl.k_compete, wl.n_head_forced, wl.n_tail_forced,
-                       wl.rank, d.proj, wl.lse_scale)
+                       wl.rank, d.proj, wl.lse_scale, wl.n_probe)
     kv_bytes = d.k.numel() * d.k.element_size() * 2
     R = int(max(2, min(args.copies, -(-CONFIG_COPIES_BYTES // kv_bytes))))
     copies = []
@@ -387,6 +388,10 @@ def config_line(name, args):
     sa.sa_decode_step(qs[0], kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws, sel, num)
     torch.cuda.synchronize()
     nb = synth.step_bytes(wl, num.cpu().numpy())
+    # the same step on the workload's own query (its needles are planted for it): recall
+    sa.sa_decode_step(d.q, kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws, sel, num)
+    torch.cuda.synchronize()
+    quality = selection_quality(wl, sel.cpu().numpy(), num.cpu().numpy())
     dws = sa.alloc_workspace(sa.sa_attn_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.max_pages, 0), dev)
     dense_us = graph_us(lambda i: sa.sa_sparse_decode_attn(qs[i % NQ], copies[i % R][0], seqs, None,
                                                            None, wl.softmax_scale, out, dws),
@@ -397,7 +402,8 @@ def config_line(name, args):
         "metric": f"decode-step µs + effective HBM GB/s, {wl.name}",
         "workload": wl.name, "batch": wl.B, "num_q_heads": wl.Hq, "num_kv_heads": wl.Hkv,
         "context": [int(x) for x in np.unique(wl.seq_lens)][:4], "kv_dtype": wl.kv_dtype,
-        "scoring": "quest min/max bound" if wl.mode == "quest" else "sals int4 index + block lse",
+        "scoring": {"quest": "quest min/max bound", "sals": "sals int4 index + block lse",
+                    "probe": f"probe sampling, {wl.n_probe} keys per {wl.unit_tokens}-token block"}[wl.mode],
         "kept_units": int(wl.n_head_forced + wl.k_compete + wl.n_tail_forced),
         "step_us": round(step_us, 2), "step_bytes": nb["total"],
         "bytes": {k2: int(v2) for k2, v2 in nb.items()},
@@ -405,12 +411,46 @@ def config_line(name, args):
         "dense_us": round(dense_us, 2),
         "dense_gbs": round(dense_b / (dense_us * 1e-6) / 1e9, 1),
         "speedup_vs_dense": round(dense_us / step_us, 2),
-        "layer_copies_rotated": R, "steps": K, "setup_s": round(setup_s, 1),
+        "layer_copies_rotated": R, "steps": K, "setup_s": round(setup_s, 1), **quality,
         "timing": "HIP graph of K steps, replayed once between two events",
     }
     print(json.dumps(rec), flush=True)
     del copies, d, ws, dws
     torch.cuda.empty_cache()
+
+
+def selection_quality(wl, sel, num):
+    """Needle recall (share of the planted keys whose page the step kept) and top-10
+    recall (share of each query head's ten largest exact logits q . k_t over the whole
+    sequence whose page the step kept), from the page lists of a step run on the
+    workload's own query.  The logits are scored on the host, so the top-10 figure is
+    given only where B * Hq * L <= 2^21."""
+    import numpy as np
+
+    import synth
+
+    kept = [[set(sel[b, h, :num[b, h]].tolist()) for h in range(wl.Hkv)] for b in range(wl.B)]
+    res = {}
+    if wl.needles:
+        res["needle_recall"] = round(sum(1 for (b, h, p, s) in wl.needles if p in kept[b][h]) /
+                                     len(wl.needles), 4)
+    if wl.kv_dtype != "i8" and wl.B * wl.Hq * int(wl.seq_lens.max()) <= 1 << 21:
+        q = (synth.bf16_to_f32(wl.q) if wl.q_dtype == "bf16" else wl.q).astype(np.float32)
+        hits = total = 0
+        for b in range(wl.B):
+            L = int(wl.seq_lens[b])
+            t = np.arange(L)
+            pp, sl = wl.page_table[b, t // 16], t % 16
+            for h in range(wl.Hkv):
+                kk = wl.k[pp, sl, h]
+                kk = (synth.bf16_to_f32(kk) if wl.kv_dtype == "bf16" else kk).astype(np.float32)
+                for g in range(wl.G):
+                    z = kk @ q[b, h * wl.G + g]
+                    top = np.argpartition(-z, 10)[:10] if L > 10 else t
+                    hits += sum(1 for x in top if (x // 16) in kept[b][h])
+                    total += len(top)
+        res["top10_recall"] = round(hits / total, 4)
+    return res
 
 
 def append_line(name, args):

@@ -70,7 +70,7 @@ typedef enum sa_status {
 } sa_status;
 
 enum { SA_F32 = 0, SA_BF16 = 1, SA_I8 = 2 };      /* element types */
-enum { SA_MODE_QUEST = 0, SA_MODE_SALS = 1 };     /* scoring modes */
+enum { SA_MODE_QUEST = 0, SA_MODE_SALS = 1, SA_MODE_PROBE = 2 };  /* scoring modes */
 
 /* Paged KV cache of one layer. */
 typedef struct sa_kv_cache {
@@ -95,14 +95,15 @@ typedef struct sa_seqs {
 
 /* How units are scored and selected. */
 typedef struct sa_select_cfg {
-  int32_t mode;          /* SA_MODE_QUEST or SA_MODE_SALS */
-  int32_t unit_tokens;   /* tokens per selection unit: 16 for QUEST (one page); multiple of 16 for SALS (64) */
+  int32_t mode;          /* SA_MODE_QUEST, SA_MODE_SALS or SA_MODE_PROBE */
+  int32_t unit_tokens;   /* tokens per selection unit: 16 for QUEST (one page); multiple of 16 for SALS (64) and PROBE (32) */
   int32_t k_compete;     /* units chosen by score among the non-forced units (>= 0) */
   int32_t n_head_forced; /* leading units always kept (QUEST: 1, the sink page) */
   int32_t n_tail_forced; /* trailing units always kept (QUEST: 1, the recent page; SALS: 2 tail blocks) */
   int32_t rank;          /* SALS: width r of the low-rank index key; must be 16. QUEST: ignored */
   const float *proj;     /* SALS: device [head_dim, rank] fp32 projection P. QUEST: NULL */
   float lse_scale;       /* SALS: temperature tau of the block LSE (typically 1/sqrt(head_dim)) */
+  int32_t n_probe;       /* PROBE: keys probed per block (>= 1; 8 in [RK]). Others: ignored */
 } sa_select_cfg;
 
 /* Library version (monotonic integer). */
@@ -182,6 +183,12 @@ int32_t sa_max_units(const sa_seqs *seqs, const sa_select_cfg *cfg);
  * unit count are not written).
  *  QUEST [Quest, criticality estimation + GQA]: score = max over the G query
  *        heads g of the group of sum_i max(q_gi * m_i, q_gi * M_i).
+ *  PROBE [RK probe signal]: block u covers [u*U, min((u+1)*U, L)) with len
+ *        tokens; step = max(1, len / n_probe); score = max over the probed
+ *        positions u*U, u*U + step, ... (< block end) and over the group's G
+ *        query heads of q_g . k_t (unscaled).  Reads K itself (no metadata:
+ *        meta and meta_scale may be NULL, sa_meta_bytes is 0 and
+ *        sa_build_page_meta does nothing).
  *  SALS  [SALS QSI steps 1-3]: qbar = mean of the group's G query heads;
  *        qt = qbar * P; s_t = scale_t * sum_j qt_j * c_tj per token;
  *        score_u = ln sum over the valid tokens t of block u of exp(lse_scale * s_t).

@@ -25,7 +25,7 @@ LIB_PATH = os.path.join(_HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE_TOO_SMALL, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16, SA_I8 = 0, 1, 2
-SA_MODE_QUEST, SA_MODE_SALS = 0, 1
+SA_MODE_QUEST, SA_MODE_SALS, SA_MODE_PROBE = 0, 1, 2
 
 _lib = None
 
@@ -52,7 +52,7 @@ class sa_select_cfg(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("unit_tokens", ctypes.c_int32),
                 ("k_compete", ctypes.c_int32), ("n_head_forced", ctypes.c_int32),
                 ("n_tail_forced", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("proj", ctypes.c_void_p), ("lse_scale", ctypes.c_float)]
+                ("proj", ctypes.c_void_p), ("lse_scale", ctypes.c_float), ("n_probe", ctypes.c_int32)]
 
 
 EXPORTS = ["sa_version", "sa_status_string", "sa_meta_bytes", "sa_meta_scale_bytes",
@@ -162,10 +162,12 @@ class SelectCfg:
     rank: int = 16
     proj: Optional[torch.Tensor] = None  # fp32 [128, rank] (SALS)
     lse_scale: float = 0.0
+    n_probe: int = 8                      # keys probed per block (PROBE)
 
     def struct(self) -> sa_select_cfg:
         return sa_select_cfg(self.mode, self.unit_tokens, self.k_compete, self.n_head_forced,
-                             self.n_tail_forced, self.rank, _ptr(self.proj), self.lse_scale)
+                             self.n_tail_forced, self.rank, _ptr(self.proj), self.lse_scale,
+                             self.n_probe)
 
 
 # ---------------------------------------------------------------- sizes
@@ -200,6 +202,8 @@ def alloc_meta(kv: KVCache, cfg: SelectCfg):
     """Device buffers for sa_build_page_meta: (meta, meta_scale or None)."""
     dev = kv.k.device
     P, S, Hkv, d = kv.k.shape
+    if cfg.mode == SA_MODE_PROBE:  # scores read K itself: no metadata
+        return None, None
     if cfg.mode == SA_MODE_QUEST:
         return torch.empty((Hkv, P, 2, d), dtype=kv.k.dtype, device=dev), None
     return (torch.empty((P, S, Hkv, cfg.rank // 2), dtype=torch.uint8, device=dev),

@@ -37,7 +37,8 @@ int check_seqs(const sa_seqs* s) {
 // Fields that selection alone uses (sa_topk_pages, list sizes).
 int check_select(const sa_select_cfg* c) {
   if (!c) return SA_ERR_INVALID_ARG;
-  if (c->mode != SA_MODE_QUEST && c->mode != SA_MODE_SALS) return SA_ERR_INVALID_ARG;
+  if (c->mode != SA_MODE_QUEST && c->mode != SA_MODE_SALS && c->mode != SA_MODE_PROBE)
+    return SA_ERR_INVALID_ARG;
   if (c->k_compete < 0 || c->n_head_forced < 0 || c->n_tail_forced < 0) return SA_ERR_INVALID_ARG;
   if ((long long)c->k_compete + c->n_head_forced + c->n_tail_forced < 1) return SA_ERR_INVALID_ARG;
   if ((long long)c->k_compete + c->n_head_forced + c->n_tail_forced > 0x3FFFFFFLL) return SA_ERR_INVALID_ARG;
@@ -55,6 +56,7 @@ int check_cfg(const sa_select_cfg* c) {
     if (c->rank != kRank) return SA_ERR_UNSUPPORTED;
     if (!(c->lse_scale == c->lse_scale)) return SA_ERR_INVALID_ARG;  // NaN
   }
+  if (c->mode == SA_MODE_PROBE && c->n_probe < 1) return SA_ERR_INVALID_ARG;
   return SA_OK;
 }
 
@@ -185,6 +187,7 @@ const char* sa_status_string(int status) {
 
 size_t sa_meta_bytes(const sa_kv_cache* kv, const sa_select_cfg* cfg) {
   if (check_kv(kv) != SA_OK || check_cfg(cfg) != SA_OK) return 0;
+  if (cfg->mode == SA_MODE_PROBE) return 0;
   if (cfg->mode == SA_MODE_QUEST) {
     if (kv->dtype == SA_I8) return 0;
     const size_t es = kv->dtype == SA_F32 ? 4 : 2;
@@ -195,7 +198,7 @@ size_t sa_meta_bytes(const sa_kv_cache* kv, const sa_select_cfg* cfg) {
 
 size_t sa_meta_scale_bytes(const sa_kv_cache* kv, const sa_select_cfg* cfg) {
   if (check_kv(kv) != SA_OK || check_cfg(cfg) != SA_OK) return 0;
-  if (cfg->mode == SA_MODE_QUEST) return 0;
+  if (cfg->mode != SA_MODE_SALS) return 0;
   return (size_t)kv->num_pages * kPage * kv->num_kv_heads * sizeof(uint16_t);
 }
 
@@ -214,6 +217,7 @@ int sa_build_page_meta(const sa_kv_cache* kv, const sa_seqs* seqs, const sa_sele
   int rc;
   if ((rc = check_kv(kv)) || (rc = check_seqs(seqs)) || (rc = check_cfg(cfg))) return rc;
   if ((rc = check_mode_kv(cfg, kv))) return rc;
+  if (cfg->mode == SA_MODE_PROBE) return SA_OK;  // no metadata: the scores read K
   if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
   const Shapes s = shapes_of(kv->num_kv_heads, kv, seqs);
   hipStream_t st = static_cast<hipStream_t>(stream);
@@ -233,7 +237,7 @@ int sa_append_kv(const void* k_new, const void* v_new, const uint16_t* k_scale_n
   if ((rc = check_mode_kv(cfg, kv))) return rc;
   if (!k_new || !v_new || !aligned16(k_new) || !aligned16(v_new)) return SA_ERR_INVALID_ARG;
   if (kv->dtype == SA_I8 && (!k_scale_new || !v_scale_new)) return SA_ERR_INVALID_ARG;
-  if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
+  if (cfg->mode != SA_MODE_PROBE && (!meta || !aligned16(meta))) return SA_ERR_INVALID_ARG;
   if (cfg->mode == SA_MODE_SALS && !meta_scale) return SA_ERR_INVALID_ARG;
   const Shapes s = shapes_of(kv->num_kv_heads, kv, seqs);
   // the cache buffers are written: the struct's pointers are const for the
@@ -252,9 +256,14 @@ int sa_score_pages(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if ((rc = check_kv(kv)) || (rc = check_seqs(seqs)) || (rc = check_cfg(cfg))) return rc;
   if ((rc = check_q(q, q_dtype, num_q_heads, kv->num_kv_heads))) return rc;
   if ((rc = check_mode_kv(cfg, kv))) return rc;
-  if (!meta || !aligned16(meta) || !scores) return SA_ERR_INVALID_ARG;
+  if (!scores) return SA_ERR_INVALID_ARG;
   const Shapes s = shapes_of(num_q_heads, kv, seqs);
   hipStream_t st = static_cast<hipStream_t>(stream);
+  if (cfg->mode == SA_MODE_PROBE)
+    return hip_status(launch_probe_score(kv->dtype, q_dtype, q, kv->k, kv->k_scale, s,
+                                         seqs->page_table, seqs->seq_lens, cfg->unit_tokens,
+                                         cfg->n_probe, scores, max_units_of(seqs, cfg), st));
+  if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
   if (cfg->mode == SA_MODE_QUEST)
     return hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
                                          seqs->seq_lens, scores, st));
@@ -326,7 +335,7 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
   const StepLayout lay = step_layout(num_q_heads, kv, seqs, cfg);
   if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
-  if (!lay.dense) {
+  if (!lay.dense && cfg->mode != SA_MODE_PROBE) {
     if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
     if (cfg->mode == SA_MODE_SALS && !meta_scale) return SA_ERR_INVALID_ARG;
   }
@@ -386,6 +395,10 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if (cfg->mode == SA_MODE_QUEST)
     rc = hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
                                        seqs->seq_lens, scores, st));
+  else if (cfg->mode == SA_MODE_PROBE)
+    rc = hip_status(launch_probe_score(kv->dtype, q_dtype, q, kv->k, kv->k_scale, s,
+                                       seqs->page_table, seqs->seq_lens, cfg->unit_tokens,
+                                       cfg->n_probe, scores, lay.max_units, st));
   else
     rc = hip_status(launch_sals_score(q_dtype, q, static_cast<const uint8_t*>(meta), meta_scale,
                                       cfg->proj, s, seqs->page_table, seqs->seq_lens,

@@ -190,6 +190,10 @@ hipError_t launch_append(int dtype, int mode, const void* k_new, const void* v_n
                          uint16_t* k_scale, uint16_t* v_scale, const Shapes& s, const int32_t* pt,
                          const int32_t* lens, const float* proj, void* meta, uint16_t* meta_scale,
                          hipStream_t st);
+hipError_t launch_probe_score(int kv_dtype, int q_dtype, const void* q, const void* k,
+                              const uint16_t* k_scale, const Shapes& s, const int32_t* pt,
+                              const int32_t* lens, int unit_tokens, int n_probe, float* scores,
+                              int max_units, hipStream_t st);
 hipError_t launch_quest_score(int kv_dtype, int q_dtype, const void* q, const void* meta,
                               const Shapes& s, const int32_t* pt, const int32_t* lens,
                               float* scores, hipStream_t st);

@@ -168,8 +168,9 @@ __global__ __launch_bounds__(256) void sals_index_kernel(
 // K/V rows (and int8 scales) are copied into slot t % 16 of its page, then
 // the page's metadata takes the token: QUEST folds it into (M, m) with the
 // comparisons quest_meta_kernel folds with (slot 0 starts the page); SALS
-// writes the token's index key, computed as sals_key does.
-template <int DT, bool SALS>
+// writes the token's index key, computed as sals_key does.  META: 0 = no
+// metadata (probe sampling reads K itself), 1 = QUEST, 2 = SALS.
+template <int DT, int META>
 __global__ __launch_bounds__(256) void append_kernel(
     const void* __restrict__ k_new, const void* __restrict__ v_new,
     const uint16_t* __restrict__ ks_new, const uint16_t* __restrict__ vs_new, void* k_, void* v_,
@@ -177,6 +178,7 @@ __global__ __launch_bounds__(256) void append_kernel(
     const int32_t* __restrict__ lens, int max_pages, const float* __restrict__ proj, void* meta_,
     uint16_t* meta_scale) {
   constexpr int ES = DT == SA_F32 ? 4 : DT == SA_BF16 ? 2 : 1;  // element bytes
+  constexpr bool SALS = META == 2;
   __shared__ float P[SALS ? kHeadDim * kRank : 1];
   const int b = blockIdx.x;
   const int L = lens[b];
@@ -230,7 +232,7 @@ __global__ __launch_bounds__(256) void append_kernel(
       if ((j & 7) == 0) reinterpret_cast<uint32_t*>(static_cast<uint8_t*>(meta_) + r * (kRank / 2))[j >> 3] = w;
       if (j == 0) meta_scale[r] = __builtin_bit_cast(uint16_t, sh);
     }
-  } else if constexpr (DT != SA_I8) {
+  } else if constexpr (META == 1 && DT != SA_I8) {
     char* meta = static_cast<char*>(meta_);
     for (int c = threadIdx.x; c < row / 8; c += blockDim.x) {
       const int h = c / (kHeadDim / 8), i0 = (c % (kHeadDim / 8)) * 8;
@@ -294,21 +296,23 @@ hipError_t launch_append(int dtype, int mode, const void* k_new, const void* v_n
                          uint16_t* k_scale, uint16_t* v_scale, const Shapes& s, const int32_t* pt,
                          const int32_t* lens, const float* proj, void* meta, uint16_t* meta_scale,
                          hipStream_t st) {
-#define SA_AP(DT, SALS)                                                                          \
-  hipLaunchKernelGGL((append_kernel<DT, SALS>), dim3(s.B), dim3(256), 0, st, k_new, v_new, ks_new, \
+#define SA_AP(DT, META)                                                                          \
+  hipLaunchKernelGGL((append_kernel<DT, META>), dim3(s.B), dim3(256), 0, st, k_new, v_new, ks_new, \
                      vs_new, k, v, k_scale, v_scale, s.num_pages, s.Hkv, pt, lens, s.max_pages,   \
                      proj, meta, meta_scale)
-  const bool sals = mode == SA_MODE_SALS;
-  switch (dtype) {
-    case SA_F32:
-      if (sals) SA_AP(SA_F32, true); else SA_AP(SA_F32, false);
-      break;
-    case SA_BF16:
-      if (sals) SA_AP(SA_BF16, true); else SA_AP(SA_BF16, false);
-      break;
-    default:
-      SA_AP(SA_I8, true);  // QUEST metadata is not kept for int8 caches
+#define SA_AP_M(DT)                                     \
+  switch (mode) {                                       \
+    case SA_MODE_QUEST: SA_AP(DT, 1); break;            \
+    case SA_MODE_SALS: SA_AP(DT, 2); break;             \
+    default: SA_AP(DT, 0);                              \
   }
+  switch (dtype) {
+    case SA_F32: SA_AP_M(SA_F32) break;
+    case SA_BF16: SA_AP_M(SA_BF16) break;
+    default:  // QUEST metadata is not kept for int8 caches
+      if (mode == SA_MODE_SALS) SA_AP(SA_I8, 2); else SA_AP(SA_I8, 0);
+  }
+#undef SA_AP_M
 #undef SA_AP
   return hipGetLastError();
 }

@@ -381,6 +381,77 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
   }
 }
 
+constexpr int kProbeUnitsPerWG = 4;  // one block per wave
+
+// Probe sampling [RK, the probe signal of the block selector]: the score of
+// block u is the largest q_g . k_t over its probed positions t (step =
+// max(1, len / n_probe) from the block start) and the group's query heads g.
+// grid (ceil(max_units / 4), Hkv, B), block 256: the group's query rows are
+// staged in LDS as fp32; wave w takes block blockIdx.x * 4 + w.  Lanes are
+// (probe slot of 8, dimension group of 8 x 16): each round reads up to eight
+// probed key rows (16 dimensions per lane), sums each slot's partial dots over
+// its eight lanes by DPP, and keeps the maximum; the eight slots are merged by
+// a row maximum and two lane swaps.  int8 keys: the dot of the codes times the
+// token's scale.
+template <int KT, int QT, int G>
+__global__ __launch_bounds__(256) void probe_score_kernel(
+    const void* __restrict__ q, int hq, const void* __restrict__ k,
+    const uint16_t* __restrict__ k_scale, int num_pages, int hkv, const int32_t* __restrict__ pt,
+    const int32_t* __restrict__ lens, int max_pages, int unit_tokens, int n_probe,
+    float* __restrict__ scores, int max_units) {
+  __shared__ float qs[G][kHeadDim];
+  const int h = blockIdx.y, b = blockIdx.z;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  for (int i = tid; i < G * kHeadDim; i += 256) {
+    const size_t qi = ((size_t)b * hq + (size_t)h * G + i / kHeadDim) * kHeadDim + i % kHeadDim;
+    qs[i / kHeadDim][i % kHeadDim] = QT == SA_F32 ? static_cast<const float*>(q)[qi]
+                                                  : bf16_to_f32(static_cast<const uint16_t*>(q)[qi]);
+  }
+  __syncthreads();
+  const int L = clamp_len(lens[b], max_pages);
+  const int nu = (L + unit_tokens - 1) / unit_tokens;
+  const int u = blockIdx.x * kProbeUnitsPerWG + wave;
+  if (u >= nu) return;  // wave-uniform, and no barrier follows
+  const int t0 = u * unit_tokens, t1 = min(t0 + unit_tokens, L);
+  const int step = max(1, (t1 - t0) / n_probe);
+  const int ns = (t1 - t0 + step - 1) / step;  // probed positions
+  const int slot = lane >> 3, dg = lane & 7;
+  const int32_t* pt_row = pt + (size_t)b * max_pages;
+  float best = -INFINITY;
+  for (int i0 = 0; i0 < ns; i0 += 8) {
+    const int i = i0 + slot;
+    const bool valid = i < ns;
+    const int t = t0 + (valid ? i : 0) * step;
+    const int pp = pt_row[t >> 4];
+    const bool ok = valid && pp >= 0 && pp < num_pages;
+    const size_t row = ((size_t)(ok ? pp : 0) * kPage + (t & 15)) * hkv + h;
+    float x[16];
+    {
+      float a[8], c[8];
+      load8<KT>(k, row * kHeadDim + 16 * dg, a);
+      load8<KT>(k, row * kHeadDim + 16 * dg + 8, c);
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = a[e];
+        x[8 + e] = c[e];
+      }
+    }
+    const float sc = KT == SA_I8 ? f16_to_f32(k_scale[row]) : 1.0f;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+      float dot = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 16; ++e) dot = fmaf(qs[g][16 * dg + e], x[e], dot);
+      dot += dpp_f32<kDppXor1>(dot);
+      dot += dpp_f32<kDppXor2>(dot);
+      dot += dpp_f32<kDppHalfMirror>(dot);
+      if (ok) best = fmaxf(best, dot * sc);
+    }
+  }
+  best = pair32_max(pair16_max(max16(best)));
+  if (lane == 0) scores[((size_t)b * hkv + h) * max_units + u] = best;
+}
+
 template <int KT, int QT>
 hipError_t quest_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, const void* meta,
                             const Shapes& s, const int32_t* pt, const int32_t* lens,
@@ -454,6 +525,42 @@ hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,
   }
 #undef SA_SG
 #undef SA_SS
+  return hipGetLastError();
+}
+
+hipError_t launch_probe_score(int kv_dtype, int q_dtype, const void* q, const void* k,
+                              const uint16_t* k_scale, const Shapes& s, const int32_t* pt,
+                              const int32_t* lens, int unit_tokens, int n_probe, float* scores,
+                              int max_units, hipStream_t st) {
+  const dim3 grid((max_units + kProbeUnitsPerWG - 1) / kProbeUnitsPerWG, s.Hkv, s.B);
+#define SA_PR(KT, QT, GG)                                                                       \
+  hipLaunchKernelGGL((probe_score_kernel<KT, QT, GG>), grid, dim3(256), 0, st, q, s.Hq, k,      \
+                     k_scale, s.num_pages, s.Hkv, pt, lens, s.max_pages, unit_tokens, n_probe,  \
+                     scores, max_units)
+#define SA_PR_G(KT, QT)                 \
+  switch (s.Hq / s.Hkv) {               \
+    case 1: SA_PR(KT, QT, 1); break;    \
+    case 2: SA_PR(KT, QT, 2); break;    \
+    case 4: SA_PR(KT, QT, 4); break;    \
+    case 8: SA_PR(KT, QT, 8); break;    \
+    default: SA_PR(KT, QT, 16); break;  \
+  }
+#define SA_PR_Q(KT)                          \
+  if (q_dtype == SA_F32) {                   \
+    SA_PR_G(KT, SA_F32)                      \
+  } else {                                   \
+    SA_PR_G(KT, SA_BF16)                     \
+  }
+  if (kv_dtype == SA_F32) {
+    SA_PR_Q(SA_F32)
+  } else if (kv_dtype == SA_BF16) {
+    SA_PR_Q(SA_BF16)
+  } else {
+    SA_PR_Q(SA_I8)
+  }
+#undef SA_PR_Q
+#undef SA_PR_G
+#undef SA_PR
   return hipGetLastError();
 }
 

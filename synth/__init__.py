@@ -337,8 +337,10 @@ CONFIG_NAMES = {
 }
 
 
-def make_config(cfg: int, layer_copy: int = 0, dense: bool = False) -> Workload:
-    """The five reference workloads at full size.  seed = 1000*cfg + layer_copy."""
+def make_config(cfg: int, layer_copy: int = 0, dense: bool = False, probe: bool = False) -> Workload:
+    """The five reference workloads at full size.  seed = 1000*cfg + layer_copy.
+    probe: the same inputs selected by probe sampling instead (32-token blocks, 8 probes,
+    the same token budget: budget/32 - 1 blocks by score plus the last block)."""
     seed = 1000 * cfg + layer_copy
     d = HEAD_DIM
     if cfg == 1:
@@ -390,6 +392,13 @@ def make_config(cfg: int, layer_copy: int = 0, dense: bool = False) -> Workload:
                          budget_pages=4096 // PAGE, seed=seed, name="cfg5")
     else:
         raise ValueError(cfg)
+    if probe:
+        budget = (wl.k_compete + wl.n_head_forced + wl.n_tail_forced) * wl.unit_tokens
+        wl.mode, wl.unit_tokens, wl.n_probe = "probe", 32, 8
+        wl.n_head_forced, wl.n_tail_forced = 0, 1
+        wl.k_compete = budget // 32 - 1
+        wl.proj = None
+        wl.name += "-probe"
     if dense:
         wl.k_compete = wl.max_units
         wl.name += "-dense"
@@ -415,7 +424,8 @@ def step_bytes(wl: Workload, num_sel: Optional[np.ndarray] = None) -> dict:
 
     meta    : Quest min/max metadata of every page of every sequence (2*d values in the
               KV dtype per page and kv-head), or the SALS index key of every token
-              (rank/2 code bytes + 2 scale bytes per token and kv-head, whole pages);
+              (rank/2 code bytes + 2 scale bytes per token and kv-head, whole pages), or the
+              probed key rows of every block (probe sampling);
     kv      : K and V of the selected pages (16 tokens each), plus int8 scales;
     q / out : the query (q dtype) and the fp32 output.
     Score and partial-result traffic is not counted."""
@@ -423,6 +433,14 @@ def step_bytes(wl: Workload, num_sel: Optional[np.ndarray] = None) -> dict:
     npages = np.array([wl.n_pages(b) for b in range(wl.B)], dtype=np.int64)
     if wl.mode == "quest":
         meta = int(npages.sum()) * wl.Hkv * 2 * wl.d * e
+    elif wl.mode == "probe":  # the probed key rows of every block (n_probe per full block)
+        meta = 0
+        for b in range(wl.B):
+            L = int(wl.seq_lens[b])
+            for t0 in range(0, L, wl.unit_tokens):
+                n = min(wl.unit_tokens, L - t0)
+                step = max(1, n // wl.n_probe)
+                meta += -(-n // step) * wl.Hkv * wl.d * e
     else:
         meta = int(npages.sum()) * PAGE * wl.Hkv * (wl.rank // 2 + 2)
     if num_sel is None:

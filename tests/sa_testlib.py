@@ -36,9 +36,9 @@ class GpuCase:
         self.d = synth.to_device(wl, self.dev)
         self.kv = sa.KVCache(self.d.k, self.d.v, self.d.k_scale, self.d.v_scale)
         self.seqs = sa.Seqs(self.d.page_table, self.d.seq_lens)
-        mode = sa.SA_MODE_QUEST if wl.mode == "quest" else sa.SA_MODE_SALS
+        mode = {"quest": sa.SA_MODE_QUEST, "sals": sa.SA_MODE_SALS, "probe": sa.SA_MODE_PROBE}[wl.mode]
         self.cfg = sa.SelectCfg(mode, wl.unit_tokens, wl.k_compete, wl.n_head_forced,
-                                wl.n_tail_forced, wl.rank, self.d.proj, wl.lse_scale)
+                                wl.n_tail_forced, wl.rank, self.d.proj, wl.lse_scale, wl.n_probe)
         self.meta = self.meta_scale = None
 
     # -- steps -------------------------------------------------------------
@@ -95,6 +95,8 @@ def np_u16(t: torch.Tensor) -> np.ndarray:
 
 def meta_np(case: GpuCase):
     m = case.meta
+    if case.wl.mode == "probe":  # no metadata: the scores read K
+        return None, None
     if case.wl.mode == "quest":
         return (m.cpu().numpy() if m.dtype == torch.float32 else np_u16(m)), None
     return m.cpu().numpy(), np_u16(case.meta_scale)

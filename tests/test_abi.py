@@ -195,3 +195,18 @@ def test_append_argument_checks():
     assert call(i8, sals, mscale=FAKE) == sa.SA_ERR_INVALID_ARG              # int8 rows need their scales
     assert call(_kv(), sals) == sa.SA_ERR_INVALID_ARG                        # SALS needs meta_scale
     assert call(_kv(num_kv_heads=3), sals, mscale=FAKE) == sa.SA_ERR_UNSUPPORTED
+
+
+def test_probe_mode_checks():
+    lib = _lib()
+    kv, seqs = _kv(), _seqs()
+    probe = _cfg(mode=sa.SA_MODE_PROBE, unit_tokens=32, k_compete=6, n_head_forced=0,
+                 n_tail_forced=1, n_probe=8)
+    assert lib.sa_meta_bytes(ctypes.byref(kv), ctypes.byref(probe)) == 0
+    assert lib.sa_meta_scale_bytes(ctypes.byref(kv), ctypes.byref(probe)) == 0
+    assert lib.sa_max_units(ctypes.byref(seqs), ctypes.byref(probe)) == 16
+    # no metadata to build: success without a launch, even with no buffers
+    assert lib.sa_build_page_meta(ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(probe), None, None, None) == sa.SA_OK
+    assert _score(lib, kv, seqs, _cfg(mode=sa.SA_MODE_PROBE, unit_tokens=32, n_probe=0)) == sa.SA_ERR_INVALID_ARG
+    assert _score(lib, kv, seqs, _cfg(mode=sa.SA_MODE_PROBE, unit_tokens=24, n_probe=8)) == sa.SA_ERR_INVALID_ARG
+    assert _score(lib, kv, seqs, probe, scores=None) == sa.SA_ERR_INVALID_ARG

@@ -36,6 +36,16 @@ CASES = {
     # many lists x pages, B = 2, ragged: several chunks per list and empty chunks
     "mha_bf16_b2_long": dict(B=2, Hq=16, Hkv=16, lens=(16384, 9000), kv_dtype="bf16",
                                q_dtype="bf16", budget_pages=40, page_table="random"),
+    # probe sampling: 32-token blocks with 8 probes (step 4), 64-token blocks, 16-token
+    # blocks with 5 probes (step 3: six probes), and 12 probes of 32 (step 2: two rounds)
+    "probe_bf16": dict(B=2, Hq=8, Hkv=8, lens=(2000, 777), kv_dtype="bf16", q_dtype="bf16",
+                       mode="probe", k_compete=12, page_table="random"),
+    "probe_gqa4_i8": dict(B=2, Hq=16, Hkv=4, lens=(3000, 1234), kv_dtype="i8", q_dtype="bf16",
+                          mode="probe", unit_tokens=64, k_compete=6, page_table="random"),
+    "probe_f32_u16": dict(B=1, Hq=2, Hkv=1, lens=(1500,), kv_dtype="f32", q_dtype="f32",
+                          mode="probe", unit_tokens=16, n_probe=5, k_compete=20),
+    "probe_gqa8_p12": dict(B=1, Hq=16, Hkv=2, lens=(2500,), kv_dtype="bf16", q_dtype="bf16",
+                           mode="probe", n_probe=12, k_compete=10),
     # a list of 18750 pages: the top-K that re-reads its keys from the scores
     "gqa2_bf16_18k_pages": dict(B=1, Hq=2, Hkv=1, lens=(300000,), kv_dtype="bf16",
                                 q_dtype="bf16", budget_pages=64),
@@ -55,7 +65,7 @@ def _full_check(wl, label):
         if wl.mode == "quest":  # [Hkv, P, 2, d]
             assert np.array_equal(g_meta[:, pages].view(np.uint8), o_meta[:, pages].view(np.uint8)), \
                 f"metadata differs (b={b})"
-        else:  # codes [P, S, Hkv, r/2], scales [P, S, Hkv]
+        elif wl.mode == "sals":  # codes [P, S, Hkv, r/2], scales [P, S, Hkv]
             assert np.array_equal(g_meta[pages], o_meta[pages]), f"index codes differ (b={b})"
             assert np.array_equal(g_ms[pages], o_ms[pages]), f"index scales differ (b={b})"
     # scores
