@@ -5,6 +5,7 @@ import pytest
 import torch
 
 import oracle
+import query_aware_sparse_min_amd as sa
 import synth
 from sa_testlib import (GpuCase, attn_tol, check_attention, check_scores, check_selection,
                         meta_np, oracle_rows_for_lists)
@@ -238,12 +239,17 @@ def test_topk_all_equal_and_sals_units():
     _topk_case((300 * 64, 299 * 64 + 5, 40 * 64), 300, 10, 0, 0, 64, sc)
 
 
-def test_step_graph_replays_match_eager():
+@pytest.mark.parametrize("gqa", [False, True])
+def test_step_graph_replays_match_eager(gqa):
     """The step captured in a HIP graph: every replay (with eager work between replays)
-    reproduces the eager result bit for bit; no memset nodes are involved."""
-    import query_aware_sparse_min_amd as sa
-    wl = synth.make_custom(B=1, Hq=8, Hkv=8, lens=(16 * 300 - 3,), kv_dtype="bf16", q_dtype="bf16",
-                           budget_pages=24, seed=13)
+    reproduces the eager result bit for bit; no memset nodes are involved.  MHA runs the
+    fused step; GQA-4 runs the scorer, top-K, attention and merge kernels."""
+    if gqa:
+        wl = synth.make_custom(B=2, Hq=16, Hkv=4, lens=(16 * 300 - 3, 2000), kv_dtype="bf16",
+                               q_dtype="bf16", budget_pages=24, page_table="random", seed=14)
+    else:
+        wl = synth.make_custom(B=1, Hq=8, Hkv=8, lens=(16 * 300 - 3,), kv_dtype="bf16",
+                               q_dtype="bf16", budget_pages=24, seed=13)
     c = GpuCase(wl)
     c.build_meta()
     ref_out, ref_sel, ref_num = c.step()
@@ -268,3 +274,22 @@ def test_step_graph_replays_match_eager():
         assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), f"replay {rep}: output"
         assert sa.step_error_flag(ws) == 0
         c.step()  # eager work between replays
+
+
+def test_attention_workspace_is_reusable():
+    """Three split-K attention calls on one workspace, each with a new query, equal
+    calls on fresh workspaces bit for bit (no state is carried between calls)."""
+    wl = synth.make_custom(B=2, Hq=16, Hkv=4, lens=(3000, 1200), kv_dtype="bf16", q_dtype="bf16",
+                           budget_pages=48, page_table="random", seed=12)
+    print("[gpu] attention workspace reuse", flush=True)
+    c = GpuCase(wl)
+    c.build_meta()
+    sel, num = c.topk(c.scores())
+    ws = sa.alloc_workspace(sa.sa_attn_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.max_pages,
+                                                      sel.shape[-1]), c.dev)
+    for i in range(3):
+        q = synth.fresh_q(wl, i)
+        out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), dtype=torch.float32, device=c.dev)
+        sa.sa_sparse_decode_attn(c.q(q), c.kv, c.seqs, sel, num, wl.softmax_scale, out, ws)
+        ref = c.attention(sel, num, q)
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"call {i} differs"
