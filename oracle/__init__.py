@@ -223,6 +223,42 @@ def attention(q: np.ndarray, q_dtype: str, k: np.ndarray, v: np.ndarray, kv_dtyp
 # ----------------------------------------------------------------------------
 # composed decode step (scores -> selection -> attention)
 # ----------------------------------------------------------------------------
+def quest_scores_per_head(q: np.ndarray, q_dtype: str, meta: np.ndarray, kv_dtype: str,
+                          page_table: np.ndarray, seq_lens: np.ndarray) -> Tuple[np.ndarray, np.ndarray]:
+    """Per-head Quest selection scores ([Quest] GQA section: the per-head variant, each
+    query head with its own pages): head h*G + g's own bound sum_i max(q_i m_i, q_i M_i)
+    per page, i.e. the group score of a group of one, taken head slot g at a time.
+    [B, Hq, max_pages] scores and magnitudes."""
+    q = _c(q)
+    B, Hq, d = q.shape
+    G = Hq // meta.shape[0]
+    mp = page_table.shape[1]
+    sc = np.empty((B, Hq, mp), dtype=np.float64)
+    ab = np.empty((B, Hq, mp), dtype=np.float64)
+    for g in range(G):
+        s, a = quest_scores(np.ascontiguousarray(q[:, g::G]), q_dtype, meta, kv_dtype, page_table,
+                            seq_lens)
+        sc[:, g::G], ab[:, g::G] = s, a
+    return sc, ab
+
+
+def attention_per_head(q: np.ndarray, q_dtype: str, k: np.ndarray, v: np.ndarray, kv_dtype: str,
+                       k_scale: Optional[np.ndarray], v_scale: Optional[np.ndarray],
+                       page_table: np.ndarray, seq_lens: np.ndarray, sel: np.ndarray,
+                       num_sel: np.ndarray, tau: float) -> np.ndarray:
+    """Each query head over its own pages: head h*G + g attends over sel[b, h*G + g]
+    (the attention of a group of one, head slot g at a time).  [B, Hq, d] fp32."""
+    q = _c(q)
+    B, Hq, d = q.shape
+    G = Hq // k.shape[2]
+    out = np.empty((B, Hq, d), dtype=np.float32)
+    for g in range(G):
+        out[:, g::G] = attention(np.ascontiguousarray(q[:, g::G]), q_dtype, k, v, kv_dtype, k_scale,
+                                 v_scale, page_table, seq_lens, np.ascontiguousarray(sel[:, g::G]),
+                                 np.ascontiguousarray(num_sel[:, g::G]), tau)
+    return out
+
+
 def build_meta(wl) -> Tuple[np.ndarray, Optional[np.ndarray]]:
     """Quest: (meta, None); SALS: (codes, scales); probe sampling: (None, None), it reads K."""
     if wl.mode == "probe":
