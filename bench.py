@@ -59,8 +59,8 @@ def parse():
     ap.add_argument("--configs", default="",
                     help="instead of the headline line, one line per listed workload "
                          "(1-5, 5d = config 5 with every page kept, 2p = config 2 selected by "
-                         "probe sampling, 2a / 4a = the decode-time append on config 2 / 4), "
-                         "e.g. --configs 1,3,4,5,5d,2p,2a,4a")
+                         "probe sampling, 3h = config 3 with per-head selection, 2a / 4a = the "
+                         "decode-time append on config 2 / 4), e.g. --configs 1,3,3h,4,5,5d,2p,2a,4a")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc outputs")
     return ap.parse_args()
@@ -330,13 +330,16 @@ def config_line(name, args):
     t0 = time.time()
     print(f"[bench] config {name}: generating inputs", file=sys.stderr, flush=True)
     wl = synth.make_config(int(name[0]), dense=name.endswith("d"), probe="p" in name[1:])
+    per_head = "h" in name[1:]
+    if per_head:
+        wl.name += "-per-head"
     d = synth.to_device(wl, dev)
     print(f"[bench] config {name}: inputs on the GPU after {time.time() - t0:.0f} s", file=sys.stderr,
           flush=True)
     seqs = sa.Seqs(d.page_table, d.seq_lens)
     mode = {"quest": sa.SA_MODE_QUEST, "sals": sa.SA_MODE_SALS, "probe": sa.SA_MODE_PROBE}[wl.mode]
     cfg = sa.SelectCfg(mode, wl.unit_tokens, wl.k_compete, wl.n_head_forced, wl.n_tail_forced,
-                       wl.rank, d.proj, wl.lse_scale, wl.n_probe)
+                       wl.rank, d.proj, wl.lse_scale, wl.n_probe, 1 if per_head else 0)
     kv_bytes = d.k.numel() * d.k.element_size() * 2
     R = int(max(2, min(args.copies, -(-CONFIG_COPIES_BYTES // kv_bytes))))
     copies = []
@@ -382,12 +385,20 @@ def config_line(name, args):
 
     K = max(10, min(args.steps, 100))
     step_us = graph_us(step, K)
-    num = torch.empty((wl.B, wl.Hkv), dtype=torch.int32, device=dev)
-    sel = torch.empty((wl.B, wl.Hkv, ms), dtype=torch.int32, device=dev)
+    n_lists = wl.Hq if per_head else wl.Hkv
+    num = torch.empty((wl.B, n_lists), dtype=torch.int32, device=dev)
+    sel = torch.empty((wl.B, n_lists, ms), dtype=torch.int32, device=dev)
     kv, meta, mscale = copies[0]
     sa.sa_decode_step(qs[0], kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws, sel, num)
     torch.cuda.synchronize()
-    nb = synth.step_bytes(wl, num.cpu().numpy())
+    if per_head:  # the attention reads each group's union of its heads' pages once
+        sel_np, num_np = sel.cpu().numpy(), num.cpu().numpy()
+        groups = np.array([[len(set().union(*[set(sel_np[b, h * wl.G + g, :num_np[b, h * wl.G + g]].tolist())
+                                              for g in range(wl.G)])) for h in range(wl.Hkv)]
+                           for b in range(wl.B)])
+        nb = synth.step_bytes(wl, groups)
+    else:
+        nb = synth.step_bytes(wl, num.cpu().numpy())
     # the same step on the workload's own query (its needles are planted for it): recall
     sa.sa_decode_step(d.q, kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws, sel, num)
     torch.cuda.synchronize()
@@ -424,17 +435,30 @@ def selection_quality(wl, sel, num):
     recall (share of each query head's ten largest exact logits q . k_t over the whole
     sequence whose page the step kept), from the page lists of a step run on the
     workload's own query.  The logits are scored on the host, so the top-10 figure is
-    given only where B * Hq * L <= 2^21."""
+    given only where B * Hq * L <= 2^24.  With one list per query head (per-head
+    selection) each head is judged by its own list, and the pages the group reads (the
+    union of its heads' lists) are reported relative to one list's length."""
     import numpy as np
 
     import synth
 
-    kept = [[set(sel[b, h, :num[b, h]].tolist()) for h in range(wl.Hkv)] for b in range(wl.B)]
+    per_head = sel.shape[1] == wl.Hq and wl.Hq != wl.Hkv
+    lists = [[set(sel[b, i, :num[b, i]].tolist()) for i in range(sel.shape[1])] for b in range(wl.B)]
+
+    def kept(b, head):  # the pages query head `head` attends over
+        return lists[b][head] if per_head else lists[b][head // wl.G]
+
     res = {}
+    if per_head:
+        union = [len(set().union(*lists[b][h * wl.G:(h + 1) * wl.G])) for b in range(wl.B)
+                 for h in range(wl.Hkv)]
+        longest = [max(len(lists[b][h * wl.G + g]) for g in range(wl.G)) for b in range(wl.B)
+                   for h in range(wl.Hkv)]
+        res["union_pages_per_list"] = round(float(np.mean(np.array(union) / np.array(longest))), 3)
     if wl.needles:
-        res["needle_recall"] = round(sum(1 for (b, h, p, s) in wl.needles if p in kept[b][h]) /
+        res["needle_recall"] = round(sum(1 for (b, h, p, s) in wl.needles if p in kept(b, h * wl.G)) /
                                      len(wl.needles), 4)
-    if wl.kv_dtype != "i8" and wl.B * wl.Hq * int(wl.seq_lens.max()) <= 1 << 21:
+    if wl.kv_dtype != "i8" and wl.B * wl.Hq * int(wl.seq_lens.max()) <= 1 << 24:
         q = (synth.bf16_to_f32(wl.q) if wl.q_dtype == "bf16" else wl.q).astype(np.float32)
         hits = total = 0
         for b in range(wl.B):
@@ -447,7 +471,7 @@ def selection_quality(wl, sel, num):
                 for g in range(wl.G):
                     z = kk @ q[b, h * wl.G + g]
                     top = np.argpartition(-z, 10)[:10] if L > 10 else t
-                    hits += sum(1 for x in top if (x // 16) in kept[b][h])
+                    hits += sum(1 for x in top if (x // 16) in kept(b, h * wl.G + g))
                     total += len(top)
         res["top10_recall"] = round(hits / total, 4)
     return res

@@ -104,6 +104,9 @@ typedef struct sa_select_cfg {
   const float *proj;     /* SALS: device [head_dim, rank] fp32 projection P. QUEST: NULL */
   float lse_scale;       /* SALS: temperature tau of the block LSE (typically 1/sqrt(head_dim)) */
   int32_t n_probe;       /* PROBE: keys probed per block (>= 1; 8 in [RK]). Others: ignored */
+  int32_t per_head;      /* QUEST: 1 = every query head selects its own pages (scores and page
+                            lists per query head; the attention reads the group's union once,
+                            [Quest] GQA section); 0 = one selection per group. Others: 0 */
 } sa_select_cfg;
 
 /* Library version (monotonic integer). */
@@ -180,7 +183,8 @@ int32_t sa_max_units(const sa_seqs *seqs, const sa_select_cfg *cfg);
 /*
  * sa_score_pages - one fp32 score per (b, kv-head, unit), written to
  * scores [batch, num_kv_heads, sa_max_units] (entries past each sequence's
- * unit count are not written).
+ * unit count are not written).  QUEST with per_head: one score per (b, query
+ * head, unit), scores [batch, num_q_heads, sa_max_units], each head's own bound.
  *  QUEST [Quest, criticality estimation + GQA]: score = max over the G query
  *        heads g of the group of sum_i max(q_gi * m_i, q_gi * M_i).
  *  PROBE [RK probe signal]: block u covers [u*U, min((u+1)*U, L)) with len
@@ -221,6 +225,27 @@ int sa_topk_pages(const float *scores, int32_t num_kv_heads, const sa_seqs *seqs
  * Workspace of sa_sparse_decode_attn for lists of up to max_sel pages
  * (max_sel <= 0: dense mode over max_pages pages).  0 on bad input.
  */
+/*
+ * sa_sparse_decode_attn_heads - attention with per-head selection [Quest, GQA
+ * section: each query head's own pages, and the union the group then reads].
+ * sel: [batch, num_q_heads, max_sel] logical pages, one list per query head
+ * (sa_topk_pages on per-head scores, with num_q_heads lists per sequence),
+ * num_sel [batch, num_q_heads].  Each head attends over its own pages only;
+ * the pages of a (b, kv-head) group are read once, as the union of the
+ * group's lists, which this call builds in the workspace (the union has at
+ * most min(G * max_sel, max_pages) pages).  max_pages <= 16384.  Output and
+ * the other arguments as sa_sparse_decode_attn; workspace:
+ * >= sa_attn_heads_workspace_size(...) bytes.
+ */
+int sa_sparse_decode_attn_heads(const void *q, int32_t q_dtype, int32_t num_q_heads,
+                                const sa_kv_cache *kv, const sa_seqs *seqs, const int32_t *sel,
+                                const int32_t *num_sel, int32_t max_sel, float softmax_scale,
+                                float *out, void *workspace, size_t workspace_bytes, void *stream);
+
+/* Workspace of sa_sparse_decode_attn_heads.  0 on bad input. */
+size_t sa_attn_heads_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_pages, int32_t max_sel);
+
 size_t sa_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t max_pages, int32_t max_sel);
 
@@ -254,7 +279,10 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  * Metadata must already be built (sa_build_page_meta).  When every list keeps
  * all of its units (k_compete + forced units >= sa_max_units) scoring is
  * skipped and dense attention runs.  sel / num_sel (optional, may be NULL)
- * receive the selection as sa_topk_pages writes it.
+ * receive the selection as sa_topk_pages writes it.  With per_head (QUEST),
+ * the step runs sa_score_pages -> sa_topk_pages over the query heads ->
+ * sa_sparse_decode_attn_heads, and sel / num_sel are per query head:
+ * [batch, num_q_heads, sa_max_selected] and [batch, num_q_heads].
  * Quest mode with one query head per kv-head runs as a single persistent
  * kernel whose workgroups hand work to each other through the workspace
  * (an error word, score keys and partial records, where 0 means "not written

@@ -52,12 +52,14 @@ class sa_select_cfg(ctypes.Structure):
     _fields_ = [("mode", ctypes.c_int32), ("unit_tokens", ctypes.c_int32),
                 ("k_compete", ctypes.c_int32), ("n_head_forced", ctypes.c_int32),
                 ("n_tail_forced", ctypes.c_int32), ("rank", ctypes.c_int32),
-                ("proj", ctypes.c_void_p), ("lse_scale", ctypes.c_float), ("n_probe", ctypes.c_int32)]
+                ("proj", ctypes.c_void_p), ("lse_scale", ctypes.c_float), ("n_probe", ctypes.c_int32),
+                ("per_head", ctypes.c_int32)]
 
 
 EXPORTS = ["sa_version", "sa_status_string", "sa_meta_bytes", "sa_meta_scale_bytes",
            "sa_build_page_meta", "sa_append_kv", "sa_max_units", "sa_score_pages", "sa_max_selected",
            "sa_topk_pages", "sa_attn_workspace_size", "sa_sparse_decode_attn",
+           "sa_attn_heads_workspace_size", "sa_sparse_decode_attn_heads",
            "sa_decode_step_workspace_size", "sa_decode_step"]
 
 
@@ -84,6 +86,8 @@ def load(path: str = LIB_PATH):
         "sa_topk_pages": (ctypes.c_int, [VP, I32, SQ, CF, VP, VP, VP]),
         "sa_attn_workspace_size": (SZ, [I32, I32, I32, I32, I32]),
         "sa_sparse_decode_attn": (ctypes.c_int, [VP, I32, I32, KV, SQ, VP, VP, I32, F, VP, VP, SZ, VP]),
+        "sa_attn_heads_workspace_size": (SZ, [I32, I32, I32, I32, I32]),
+        "sa_sparse_decode_attn_heads": (ctypes.c_int, [VP, I32, I32, KV, SQ, VP, VP, I32, F, VP, VP, SZ, VP]),
         "sa_decode_step_workspace_size": (SZ, [I32, KV, SQ, CF]),
         "sa_decode_step": (ctypes.c_int, [VP, I32, I32, KV, SQ, CF, VP, VP, F, VP, VP, VP, VP, SZ, VP]),
     }
@@ -163,11 +167,12 @@ class SelectCfg:
     proj: Optional[torch.Tensor] = None  # fp32 [128, rank] (SALS)
     lse_scale: float = 0.0
     n_probe: int = 8                      # keys probed per block (PROBE)
+    per_head: int = 0                     # QUEST: one selection per query head
 
     def struct(self) -> sa_select_cfg:
         return sa_select_cfg(self.mode, self.unit_tokens, self.k_compete, self.n_head_forced,
                              self.n_tail_forced, self.rank, _ptr(self.proj), self.lse_scale,
-                             self.n_probe)
+                             self.n_probe, self.per_head)
 
 
 # ---------------------------------------------------------------- sizes
@@ -190,6 +195,11 @@ def sa_max_selected(seqs: Seqs, cfg: SelectCfg) -> int:
 def sa_attn_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_pages: int,
                            max_sel: int) -> int:
     return load().sa_attn_workspace_size(batch, num_q_heads, num_kv_heads, max_pages, max_sel)
+
+
+def sa_attn_heads_workspace_size(batch: int, num_q_heads: int, num_kv_heads: int, max_pages: int,
+                                 max_sel: int) -> int:
+    return load().sa_attn_heads_workspace_size(batch, num_q_heads, num_kv_heads, max_pages, max_sel)
 
 
 def sa_decode_step_workspace_size(num_q_heads: int, kv: KVCache, seqs: Seqs, cfg: SelectCfg) -> int:
@@ -263,6 +273,17 @@ def sa_sparse_decode_attn(q: torch.Tensor, kv: KVCache, seqs: Seqs, sel: Optiona
                                         _ptr(sel), _ptr(num_sel), max_sel, softmax_scale,
                                         _ptr(out), _ptr(workspace), workspace.numel(),
                                         _stream(stream)), "sa_sparse_decode_attn")
+
+
+def sa_sparse_decode_attn_heads(q: torch.Tensor, kv: KVCache, seqs: Seqs, sel: torch.Tensor,
+                                num_sel: torch.Tensor, softmax_scale: float, out: torch.Tensor,
+                                workspace: torch.Tensor, stream=None) -> None:
+    """Attention with one page list per query head (sel [B, Hq, max_sel])."""
+    _check(load().sa_sparse_decode_attn_heads(_ptr(q), _dtype_code(q), q.shape[1],
+                                              ctypes.byref(kv.struct()), ctypes.byref(seqs.struct()),
+                                              _ptr(sel), _ptr(num_sel), sel.shape[-1], softmax_scale,
+                                              _ptr(out), _ptr(workspace), workspace.numel(),
+                                              _stream(stream)), "sa_sparse_decode_attn_heads")
 
 
 def sa_decode_step(q: torch.Tensor, kv: KVCache, seqs: Seqs, cfg: SelectCfg, meta: torch.Tensor,

@@ -57,6 +57,8 @@ int check_cfg(const sa_select_cfg* c) {
     if (!(c->lse_scale == c->lse_scale)) return SA_ERR_INVALID_ARG;  // NaN
   }
   if (c->mode == SA_MODE_PROBE && c->n_probe < 1) return SA_ERR_INVALID_ARG;
+  if (c->per_head != 0 && c->per_head != 1) return SA_ERR_INVALID_ARG;
+  if (c->per_head && c->mode != SA_MODE_QUEST) return SA_ERR_UNSUPPORTED;
   return SA_OK;
 }
 
@@ -132,13 +134,41 @@ int resident_step_wgs(int kv_dtype, int q_dtype, int max_pages) {
 
 constexpr int kPlanCUs = 256;  // task decomposition is planned for a 256-CU MI355X
 
+// Workspace of the per-head attention: the union lists and their lengths,
+// then the split-K partial records over the union.
+struct HeadsLayout {
+  size_t ulist, ucount, partials, total;
+  int umax;
+  AttnPlan plan;
+};
+
+HeadsLayout heads_layout(int B, int hq, int hkv, int max_pages, int max_sel) {
+  HeadsLayout H{};
+  const long long u = (long long)(hq / hkv) * max_sel;
+  H.umax = (int)(u < max_pages ? u : max_pages);
+  if (H.umax < 1) H.umax = 1;
+  H.plan = plan_attention(B, hq, hkv, H.umax);
+  const size_t lists = (size_t)B * hkv;
+  size_t off = 0;
+  H.ulist = off;
+  off = align_up(off + lists * H.umax * sizeof(int32_t));
+  H.ucount = off;
+  off = align_up(off + lists * sizeof(int32_t));
+  H.partials = off;
+  off = align_up(off + H.plan.partial_floats * sizeof(float));
+  H.total = off;
+  return H;
+}
+
 struct StepLayout {
-  size_t ctl, scores, sel, num_sel, partials, total;
+  size_t ctl, scores, sel, num_sel, partials, heads, total;
   int max_units, max_sel;
   bool dense;  // every list keeps all of its units: no scoring needed
   bool fused;  // Quest: one persistent kernel for the whole step
+  bool per_head;  // Quest: one selection per query head, attention over the group's union
   AttnPlan plan;
   StepPlan splan;
+  HeadsLayout hl;
 };
 
 StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa_select_cfg* c) {
@@ -146,9 +176,12 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   L.max_units = max_units_of(s, c);
   L.max_sel = max_sel_of(s, c);
   L.dense = (long long)c->k_compete + c->n_head_forced + c->n_tail_forced >= L.max_units;
-  L.fused = !L.dense && c->mode == SA_MODE_QUEST && hq / kv->num_kv_heads <= kStepMaxGroup &&
-            s->max_pages <= kStepMaxPages && kv->num_pages <= kStepMaxPhysPages;
-  const size_t lists = (size_t)s->batch * kv->num_kv_heads;
+  L.per_head = c->per_head != 0 && !L.dense;
+  L.fused = !L.dense && !L.per_head && c->mode == SA_MODE_QUEST &&
+            hq / kv->num_kv_heads <= kStepMaxGroup && s->max_pages <= kStepMaxPages &&
+            kv->num_pages <= kStepMaxPhysPages;
+  // selection lists: one per kv-head, or one per query head with per_head
+  const size_t lists = (size_t)s->batch * (L.per_head ? hq : kv->num_kv_heads);
   L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel);
   L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
   const size_t fused_part = (size_t)L.splan.lists * L.splan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2);
@@ -164,6 +197,11 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   L.partials = off;
   const size_t pf = L.plan.partial_floats > fused_part ? L.plan.partial_floats : fused_part;
   off = align_up(off + pf * sizeof(float));
+  L.heads = off;
+  if (L.per_head) {
+    L.hl = heads_layout(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel);
+    off = align_up(off + L.hl.total);
+  }
   L.total = off;
   return L;
 }
@@ -266,7 +304,7 @@ int sa_score_pages(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
   if (cfg->mode == SA_MODE_QUEST)
     return hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
-                                         seqs->seq_lens, scores, st));
+                                         seqs->seq_lens, scores, st, cfg->per_head != 0));
   if (!meta_scale) return SA_ERR_INVALID_ARG;
   return hip_status(launch_sals_score(q_dtype, q, static_cast<const uint8_t*>(meta), meta_scale,
                                       cfg->proj, s, seqs->page_table, seqs->seq_lens,
@@ -284,6 +322,39 @@ int sa_topk_pages(const float* scores, int32_t num_kv_heads, const sa_seqs* seqs
                                 cfg->unit_tokens, cfg->k_compete, cfg->n_head_forced,
                                 cfg->n_tail_forced, sel, num_sel, max_sel_of(seqs, cfg),
                                 static_cast<hipStream_t>(stream)));
+}
+
+size_t sa_attn_heads_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
+                                    int32_t max_pages, int32_t max_sel) {
+  if (batch < 1 || max_pages < 1 || max_pages > kUnionPages || max_sel < 1) return 0;
+  if (!group_ok(num_q_heads, num_kv_heads)) return 0;
+  return heads_layout(batch, num_q_heads, num_kv_heads, max_pages, max_sel).total;
+}
+
+int sa_sparse_decode_attn_heads(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                const sa_kv_cache* kv, const sa_seqs* seqs, const int32_t* sel,
+                                const int32_t* num_sel, int32_t max_sel, float softmax_scale,
+                                float* out, void* workspace, size_t workspace_bytes, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs))) return rc;
+  if ((rc = check_q(q, q_dtype, num_q_heads, kv->num_kv_heads))) return rc;
+  if (!out || !workspace || ((uintptr_t)workspace % kAlign) != 0) return SA_ERR_INVALID_ARG;
+  if (!sel || !num_sel || max_sel < 1) return SA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
+  if (seqs->max_pages > kUnionPages) return SA_ERR_UNSUPPORTED;
+  const HeadsLayout H = heads_layout(seqs->batch, num_q_heads, kv->num_kv_heads, seqs->max_pages, max_sel);
+  if (workspace_bytes < H.total) return SA_ERR_WORKSPACE_TOO_SMALL;
+  const Shapes s = shapes_of(num_q_heads, kv, seqs);
+  hipStream_t st = static_cast<hipStream_t>(stream);
+  char* ws = static_cast<char*>(workspace);
+  int32_t* ulist = reinterpret_cast<int32_t*>(ws + H.ulist);
+  int32_t* ucount = reinterpret_cast<int32_t*>(ws + H.ucount);
+  rc = hip_status(launch_union(sel, num_sel, max_sel, s, seqs->seq_lens, ulist, ucount, H.umax, st));
+  if (rc) return rc;
+  return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale, kv->v_scale,
+                                     s, seqs->page_table, seqs->seq_lens, ulist, ucount, H.umax,
+                                     H.plan, softmax_scale, reinterpret_cast<float*>(ws + H.partials),
+                                     out, st, true));
 }
 
 size_t sa_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
@@ -334,6 +405,7 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if ((sel == nullptr) != (num_sel == nullptr)) return SA_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
   const StepLayout lay = step_layout(num_q_heads, kv, seqs, cfg);
+  if (lay.per_head && seqs->max_pages > kUnionPages) return SA_ERR_UNSUPPORTED;
   if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
   if (!lay.dense && cfg->mode != SA_MODE_PROBE) {
     if (!meta || !aligned16(meta)) return SA_ERR_INVALID_ARG;
@@ -342,6 +414,8 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   char* ws = static_cast<char*>(workspace);
   hipStream_t st = static_cast<hipStream_t>(stream);
   const Shapes s = shapes_of(num_q_heads, kv, seqs);
+  Shapes s_lists = s;  // selection lists per sequence: the query heads with per_head
+  if (cfg->per_head) s_lists.Hkv = s.Hq;
   int32_t* sel_buf = sel ? sel : reinterpret_cast<int32_t*>(ws + lay.sel);
   int32_t* num_buf = num_sel ? num_sel : reinterpret_cast<int32_t*>(ws + lay.num_sel);
   float* partials = reinterpret_cast<float*>(ws + lay.partials);
@@ -349,7 +423,7 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if (lay.dense) {
     // every unit of every list is kept: selection is the identity
     if (sel) {
-      rc = hip_status(launch_topk(nullptr, lay.max_units, s, seqs->seq_lens, cfg->unit_tokens,
+      rc = hip_status(launch_topk(nullptr, lay.max_units, s_lists, seqs->seq_lens, cfg->unit_tokens,
                                   cfg->k_compete, cfg->n_head_forced, cfg->n_tail_forced, sel_buf,
                                   num_buf, lay.max_sel, st));
       if (rc) return rc;
@@ -391,6 +465,27 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
     StepPlan P = lay.splan;
     P.grid = P.n_tasks < wgs ? P.n_tasks : wgs;
     return hip_status(launch_quest_step(kv->dtype, q_dtype, A, P, st));
+  }
+  if (lay.per_head) {
+    // every query head's own bound, selection and pages; the group's union read once
+    rc = hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,
+                                       seqs->seq_lens, scores, st, true));
+    if (rc) return rc;
+    rc = hip_status(launch_topk(scores, lay.max_units, s_lists, seqs->seq_lens, cfg->unit_tokens,
+                                cfg->k_compete, cfg->n_head_forced, cfg->n_tail_forced, sel_buf,
+                                num_buf, lay.max_sel, st));
+    if (rc) return rc;
+    char* hw = ws + lay.heads;
+    int32_t* ulist = reinterpret_cast<int32_t*>(hw + lay.hl.ulist);
+    int32_t* ucount = reinterpret_cast<int32_t*>(hw + lay.hl.ucount);
+    rc = hip_status(launch_union(sel_buf, num_buf, lay.max_sel, s, seqs->seq_lens, ulist, ucount,
+                                 lay.hl.umax, st));
+    if (rc) return rc;
+    return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale,
+                                       kv->v_scale, s, seqs->page_table, seqs->seq_lens, ulist,
+                                       ucount, lay.hl.umax, lay.hl.plan, softmax_scale,
+                                       reinterpret_cast<float*>(hw + lay.hl.partials), out, st,
+                                       true));
   }
   if (cfg->mode == SA_MODE_QUEST)
     rc = hip_status(launch_quest_score(kv->dtype, q_dtype, q, meta, s, seqs->page_table,

@@ -75,6 +75,7 @@ struct Raw8<SA_I8> {
 struct PageRef {
   int pp;  // physical page, -1 if the slot is empty
   int nv;  // valid tokens
+  uint32_t mask = 0xFFFFFFFFu;  // query heads of the group that attend to the page
 };
 
 // The pages j = j0 + wave, j0 + wave + NW, ... (< j1) that one wave takes from
@@ -88,16 +89,19 @@ struct WavePages {
   const int32_t* lst;
   const int32_t* rlst;
   int j0, j1, np, num_pages, L, wave;
+  bool masked;
   int my_pp = -1, my_nv = 0;
+  uint32_t my_mask = 0xFFFFFFFFu;
 
   // jcap >= j1 bounds the list entries that may be read before j1 is known
-  // (-1: j1), so that the list read need not wait for the list length
+  // (-1: j1), so that the list read need not wait for the list length.
+  // masked: list entries are (head mask << 16) | logical page.
   __device__ __forceinline__ WavePages(const int32_t* pt_row_, const int32_t* lst_,
                                        const int32_t* rlst_, int j0_, int j1_, int L_,
-                                       int num_pages_, int jcap = -1)
+                                       int num_pages_, int jcap = -1, bool masked_ = false)
       : pt_row(pt_row_), lst(lst_), rlst(rlst_), j0(j0_), j1(j1_),
         np((L_ + kPage - 1) / kPage), num_pages(num_pages_), L(L_),
-        wave((int)(threadIdx.x >> 6)) {
+        wave((int)(threadIdx.x >> 6)), masked(masked_) {
     const int lane = threadIdx.x & 63;
     const int j = j0 + wave + NW * lane;
     if (rlst) {
@@ -110,6 +114,10 @@ struct WavePages {
       int p = -1;
       if (j < (jcap < 0 ? j1 : jcap)) p = lst ? ld_x<COH>(lst + j) : j;
       if (j >= j1) p = -1;
+      if (masked && p != -1) {
+        my_mask = (uint32_t)p >> 16;
+        p &= 0xFFFF;
+      }
       if (p >= 0 && p < np) {
         const int pp = pt_row[p];
         if (pp >= 0 && pp < num_pages) {
@@ -127,6 +135,7 @@ struct WavePages {
     if (x < 64) {
       pr.pp = __builtin_amdgcn_readlane(my_pp, x);
       pr.nv = __builtin_amdgcn_readlane(my_nv, x);
+      if (masked) pr.mask = (uint32_t)__builtin_amdgcn_readlane((int)my_mask, x);
       return pr;
     }
     if (rlst) {  // wave with more than 64 pages
@@ -137,7 +146,11 @@ struct WavePages {
       }
       return pr;
     }
-    const int p = lst ? ld_x<COH>(lst + j) : j;
+    int p = lst ? ld_x<COH>(lst + j) : j;
+    if (masked) {
+      pr.mask = (uint32_t)p >> 16;
+      p &= 0xFFFF;
+    }
     if (p < 0 || p >= np) return pr;
     const int pp = pt_row[p];
     if (pp < 0 || pp >= num_pages) return pr;
@@ -195,7 +208,7 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
                              const int32_t* __restrict__ pt_row, int L, const int32_t* lst, int j0,
                              int j1, float scale_log2, float* __restrict__ part,
                              AttnSmem<G, NW>& sm, const int32_t* rlst = nullptr,
-                             int jcap = -1) {
+                             int jcap = -1, bool masked = false) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int r = lane >> 4, c = lane & 15;
   const int hq = hkv * G;
@@ -213,7 +226,7 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
   }
 
-  const WavePages<COH, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages, jcap);
+  const WavePages<COH, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages, jcap, masked);
 
   for (int jb = j0 + wave; jb < j1; jb += NW * PW) {
     PageRef pg[PW];
@@ -242,9 +255,9 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
     for (int u = 0; u < PW; ++u) {
       // an empty slot is masked (selects, no branch, so the loads above stay
       // where they are): all its scores are -inf and it changes nothing
-      const bool live = pg[u].pp >= 0;
 #pragma unroll
       for (int g = 0; g < G; ++g) {
+        const bool live = pg[u].pp >= 0 && ((pg[u].mask >> g) & 1u);
         float z[4];
 #pragma unroll
         for (int it = 0; it < 4; ++it) {
@@ -377,7 +390,8 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
                                                   const int32_t* __restrict__ pt_row, int L,
                                                   const int32_t* lst, int j0, int j1,
                                                   float scale_log2, float* __restrict__ part,
-                                                  AttnSmem<G, NW>& sm, int jcap = -1) {
+                                                  AttnSmem<G, NW>& sm, int jcap = -1,
+                                                  bool masked = false) {
   static_assert(G >= 1 && G <= 16, "one MFMA column per query head");
   static_assert(KT == SA_BF16 || KT == SA_I8, "K enters the MFMA as bf16");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -407,7 +421,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
 
-  const WavePages<false, NW> page_of(pt_row, lst, nullptr, j0, j1, L, num_pages, jcap);
+  const WavePages<false, NW> page_of(pt_row, lst, nullptr, j0, j1, L, num_pages, jcap, masked);
   for (int jb = j0 + wave; jb < j1; jb += NW) {
     const PageRef pg = page_of(jb);
     const size_t ppl = pg.pp >= 0 ? (size_t)pg.pp : 0;  // empty slot: load page 0, result unused
@@ -436,7 +450,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk].get(), qb[kk], z, 0, 0, 0);
 
-    const bool live = pg.pp >= 0 && n < G;
+    const bool live = pg.pp >= 0 && n < G && ((pg.mask >> n) & 1u);
     float zz[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i)  // token 4 i + qg

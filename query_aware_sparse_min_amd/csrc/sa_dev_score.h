@@ -29,16 +29,18 @@ typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
 // function returns n.  sc_row: the list's scores (device-coherent stores when
 // COH; KEYS: stored as order_key() words instead of floats).  pp_out
 // (optional, LDS): the physical page of page p0 + j at [j], -1
-// when the page is invalid or its page-table entry is out of range.  All
-// 64 * NW threads call.
-template <int KT, int QT, int G, int IT, bool COH = false, int NW = 4, bool KEYS = false>
+// when the page is invalid or its page-table entry is out of range.  PH: each
+// query head's own bound instead of the group max, head g's row at
+// sc_row + g * head_stride.  All 64 * NW threads call.
+template <int KT, int QT, int G, int IT, bool COH = false, int NW = 4, bool KEYS = false,
+          bool PH = false>
 __device__ __forceinline__ int quest_score_range(const void* __restrict__ q,
                                                   const void* __restrict__ meta, int num_pages,
                                                   int hkv, int b, int h,
                                                   const int32_t* __restrict__ pt_row, int p0,
                                                   int p1, const int32_t* __restrict__ len_b,
                                                   int max_pages, float* __restrict__ sc_row,
-                                                  int32_t* pp_out = nullptr) {
+                                                  int32_t* pp_out = nullptr, int head_stride = 0) {
   constexpr bool kDot = KT == SA_BF16 && QT == SA_BF16;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int quarter = lane >> 4, row = (lane >> 3) & 1, c = lane & 7;
@@ -93,6 +95,7 @@ __device__ __forceinline__ int quest_score_range(const void* __restrict__ q,
   for (int it = 0; it < IT; ++it) {
     const bool ok = pg[it] < p1 && pg[it] < n_valid && ppg[it] >= 0 && ppg[it] < num_pages;
     float best = -INFINITY;
+    float per[PH ? G : 1];
 #pragma unroll
     for (int g = 0; g < G; ++g) {
       float s = 0.0f;
@@ -116,6 +119,14 @@ __device__ __forceinline__ int quest_score_range(const void* __restrict__ q,
       // applied to the sum (a select, not a branch), so no load is sunk
       s = sum16(s);
       best = fmaxf(best, s);
+      if constexpr (PH) per[g] = s;
+    }
+    if constexpr (PH) {
+      if ((lane & 15) == 0 && pg[it] < p1) {
+#pragma unroll
+        for (int g = 0; g < G; ++g) st_x<COH>(sc_row + (size_t)g * head_stride + pg[it], ok ? per[g] : -INFINITY);
+      }
+      continue;
     }
     if ((lane & 15) == 0 && pg[it] < p1) {
       const float sv = ok ? best : -INFINITY;

@@ -196,7 +196,7 @@ hipError_t launch_probe_score(int kv_dtype, int q_dtype, const void* q, const vo
                               int max_units, hipStream_t st);
 hipError_t launch_quest_score(int kv_dtype, int q_dtype, const void* q, const void* meta,
                               const Shapes& s, const int32_t* pt, const int32_t* lens,
-                              float* scores, hipStream_t st);
+                              float* scores, hipStream_t st, bool per_head = false);
 hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,
                              const uint16_t* scales, const float* proj, const Shapes& s,
                              const int32_t* pt, const int32_t* lens, int unit_tokens, float tau,
@@ -213,11 +213,18 @@ struct AttnPlan {
 };
 AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len);
 
+// Per-head selection: the union of a group's per-head page lists (ascending,
+// (head mask << 16) | page entries, umax per list) for the masked attention.
+constexpr int kUnionPages = 16384;  // largest max_pages the union supports
+hipError_t launch_union(const int32_t* sel, const int32_t* num_sel, int max_sel, const Shapes& s,
+                        const int32_t* lens, int32_t* ulist, int32_t* ucount, int umax,
+                        hipStream_t st);
+
 hipError_t launch_attention(int kv_dtype, int q_dtype, const void* q, const void* k,
                             const void* v, const uint16_t* k_scale, const uint16_t* v_scale,
                             const Shapes& s, const int32_t* pt, const int32_t* lens,
                             const int32_t* sel, const int32_t* num_sel, int max_sel,
                             const AttnPlan& plan, float softmax_scale, float* partials,
-                            float* out, hipStream_t st);
+                            float* out, hipStream_t st, bool masked = false);
 
 }  // namespace sa

@@ -19,8 +19,9 @@ namespace {
 constexpr int kScoreIT = 2;                        // load pairs per lane
 constexpr int kScorePagesPerWG = 16 * kScoreIT;     // 32 pages per workgroup
 
-// grid (ceil(max_pages / 32), Hkv, B), block 256
-template <int KT, int QT, int G>
+// grid (ceil(max_pages / 32), Hkv, B), block 256.  PH: one row of scores per
+// query head ([B, Hq, max_pages]) instead of one per group.
+template <int KT, int QT, int G, bool PH>
 __global__ __launch_bounds__(256) void quest_score_kernel(
     const void* __restrict__ q, const void* __restrict__ meta, int num_pages, int hkv,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
@@ -30,9 +31,10 @@ __global__ __launch_bounds__(256) void quest_score_kernel(
   const int n = (L + kPage - 1) / kPage;
   const int p0 = blockIdx.x * kScorePagesPerWG;
   if (p0 >= n) return;
-  quest_score_range<KT, QT, G, kScoreIT>(q, meta, num_pages, hkv, b, h, pt + (size_t)b * max_pages,
-                                         p0, min(p0 + kScorePagesPerWG, n), lens + b, max_pages,
-                                         scores + ((size_t)b * hkv + h) * max_pages);
+  const size_t row0 = PH ? ((size_t)b * hkv + h) * G : (size_t)b * hkv + h;
+  quest_score_range<KT, QT, G, kScoreIT, false, 4, false, PH>(
+      q, meta, num_pages, hkv, b, h, pt + (size_t)b * max_pages, p0, min(p0 + kScorePagesPerWG, n),
+      lens + b, max_pages, scores + row0 * max_pages, nullptr, max_pages);
 }
 
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
@@ -50,9 +52,10 @@ constexpr int kMfmaPagesPerWG = 4 * kMfmaTilesPerWave * 16;        // 128 pages 
 // kk, elements 32 kk + 8 (l / 16) .. + 7 of head l % 16 (A) and of page l % 16
 // of the tile (B: one 16-byte load), so each lane loads its page's 128 bytes
 // as eight 16-byte pieces.  The result tile holds heads 4 (l / 16) + i of page
-// l % 16 in lane l; the group score is their max over the G heads.
+// l % 16 in lane l; the group score is their max over the G heads (PH: each
+// head's own row of scores instead).
 // grid (ceil(max_pages / 128), Hkv, B), block 256.
-template <int G>
+template <int G, bool PH>
 __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
     const uint16_t* __restrict__ q, const uint16_t* __restrict__ meta, int num_pages, int hkv,
     const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
@@ -107,12 +110,20 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
     for (int kk = 0; kk < 8; ++kk)
       acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, aw[kk]),
                                                    __builtin_bit_cast(bf16x8_t, mw[t][kk]), acc, 0, 0, 0);
+    const bool ok = pg[t] < n_valid && pp[t] >= 0 && pp[t] < num_pages;
+    if constexpr (PH) {
+      float* head_rows = scores + ((size_t)b * hkv + h) * G * max_pages;
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+        if (4 * kg + i < G && pg[t] < n_valid)
+          head_rows[(size_t)(4 * kg + i) * max_pages + pg[t]] = ok ? acc[i] : -INFINITY;
+      continue;
+    }
     float best = -INFINITY;
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (4 * kg + i < G) best = fmaxf(best, acc[i]);
     best = pair32_max(pair16_max(best));
-    const bool ok = pg[t] < n_valid && pp[t] >= 0 && pp[t] < num_pages;
     if (kg == 0 && pg[t] < n_valid) sc_row[pg[t]] = ok ? best : -INFINITY;
   }
 }
@@ -452,12 +463,12 @@ __global__ __launch_bounds__(256) void probe_score_kernel(
   if (lane == 0) scores[((size_t)b * hkv + h) * max_units + u] = best;
 }
 
-template <int KT, int QT>
+template <int KT, int QT, bool PH>
 hipError_t quest_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, const void* meta,
                             const Shapes& s, const int32_t* pt, const int32_t* lens,
                             float* scores) {
 #define SA_QS(GG)                                                                              \
-  hipLaunchKernelGGL((quest_score_kernel<KT, QT, GG>), grid, dim3(256), 0, st, q, meta,        \
+  hipLaunchKernelGGL((quest_score_kernel<KT, QT, GG, PH>), grid, dim3(256), 0, st, q, meta,    \
                      s.num_pages, s.Hkv, pt, lens, s.max_pages, scores)
   switch (G) {
     case 1: SA_QS(1); break;
@@ -470,33 +481,48 @@ hipError_t quest_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, con
   return hipGetLastError();
 }
 
+template <int KT, int QT>
+hipError_t quest_dispatch(bool per_head, int G, dim3 grid, hipStream_t st, const void* q,
+                          const void* meta, const Shapes& s, const int32_t* pt,
+                          const int32_t* lens, float* scores) {
+  return per_head ? quest_dispatch_g<KT, QT, true>(G, grid, st, q, meta, s, pt, lens, scores)
+                  : quest_dispatch_g<KT, QT, false>(G, grid, st, q, meta, s, pt, lens, scores);
+}
+
 }  // namespace
 
 hipError_t launch_quest_score(int kv_dtype, int q_dtype, const void* q, const void* meta,
                               const Shapes& s, const int32_t* pt, const int32_t* lens,
-                              float* scores, hipStream_t st) {
+                              float* scores, hipStream_t st, bool per_head) {
   const int G = s.Hq / s.Hkv;
   dim3 grid((s.max_pages + kScorePagesPerWG - 1) / kScorePagesPerWG, s.Hkv, s.B);
   if (kv_dtype == SA_F32)
-    return q_dtype == SA_F32 ? quest_dispatch_g<SA_F32, SA_F32>(G, grid, st, q, meta, s, pt, lens, scores)
-                             : quest_dispatch_g<SA_F32, SA_BF16>(G, grid, st, q, meta, s, pt, lens, scores);
+    return q_dtype == SA_F32 ? quest_dispatch<SA_F32, SA_F32>(per_head, G, grid, st, q, meta, s, pt, lens, scores)
+                             : quest_dispatch<SA_F32, SA_BF16>(per_head, G, grid, st, q, meta, s, pt, lens, scores);
   if (q_dtype == SA_BF16 && G >= 4) {  // bf16 query groups of four or more: matrix cores
     const dim3 gm((s.max_pages + kMfmaPagesPerWG - 1) / kMfmaPagesPerWG, s.Hkv, s.B);
     const uint16_t* qh = static_cast<const uint16_t*>(q);
     const uint16_t* mh = static_cast<const uint16_t*>(meta);
-#define SA_QM(GG)                                                                               \
-  hipLaunchKernelGGL((quest_score_mfma_kernel<GG>), gm, dim3(256), 0, st, qh, mh, s.num_pages, \
+#define SA_QM(GG, PH)                                                                               \
+  hipLaunchKernelGGL((quest_score_mfma_kernel<GG, PH>), gm, dim3(256), 0, st, qh, mh, s.num_pages, \
                      s.Hkv, pt, lens, s.max_pages, scores)
-    switch (G) {
-      case 4: SA_QM(4); break;
-      case 8: SA_QM(8); break;
-      default: SA_QM(16); break;
+#define SA_QMG(PH)                  \
+  switch (G) {                      \
+    case 4: SA_QM(4, PH); break;    \
+    case 8: SA_QM(8, PH); break;    \
+    default: SA_QM(16, PH); break;  \
+  }
+    if (per_head) {
+      SA_QMG(true)
+    } else {
+      SA_QMG(false)
     }
+#undef SA_QMG
 #undef SA_QM
     return hipGetLastError();
   }
-  return q_dtype == SA_F32 ? quest_dispatch_g<SA_BF16, SA_F32>(G, grid, st, q, meta, s, pt, lens, scores)
-                           : quest_dispatch_g<SA_BF16, SA_BF16>(G, grid, st, q, meta, s, pt, lens, scores);
+  return q_dtype == SA_F32 ? quest_dispatch<SA_BF16, SA_F32>(per_head, G, grid, st, q, meta, s, pt, lens, scores)
+                           : quest_dispatch<SA_BF16, SA_BF16>(per_head, G, grid, st, q, meta, s, pt, lens, scores);
 }
 
 hipError_t launch_sals_score(int q_dtype, const void* q, const uint8_t* codes,

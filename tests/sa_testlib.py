@@ -78,10 +78,11 @@ class GpuCase:
                                 self.dev)
         out = torch.full((wl.B, wl.Hq, wl.d), float("nan"), dtype=torch.float32, device=self.dev)
         sel = num = None
-        if want_sel:
+        if want_sel:  # one list per kv-head, or per query head with per-head selection
             ms = sa.sa_max_selected(self.seqs, self.cfg)
-            sel = torch.full((wl.B, wl.Hkv, ms), -7, dtype=torch.int32, device=self.dev)
-            num = torch.full((wl.B, wl.Hkv), -7, dtype=torch.int32, device=self.dev)
+            lists = wl.Hq if self.cfg.per_head else wl.Hkv
+            sel = torch.full((wl.B, lists, ms), -7, dtype=torch.int32, device=self.dev)
+            num = torch.full((wl.B, lists), -7, dtype=torch.int32, device=self.dev)
         sa.sa_decode_step(self.q(q_np), self.kv, self.seqs, self.cfg, self.meta, self.meta_scale,
                           wl.softmax_scale, out, ws, sel, num)
         assert sa.step_error_flag(ws) == 0, "a bounded wait of the fused step timed out"

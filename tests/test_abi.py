@@ -210,3 +210,26 @@ def test_probe_mode_checks():
     assert _score(lib, kv, seqs, _cfg(mode=sa.SA_MODE_PROBE, unit_tokens=32, n_probe=0)) == sa.SA_ERR_INVALID_ARG
     assert _score(lib, kv, seqs, _cfg(mode=sa.SA_MODE_PROBE, unit_tokens=24, n_probe=8)) == sa.SA_ERR_INVALID_ARG
     assert _score(lib, kv, seqs, probe, scores=None) == sa.SA_ERR_INVALID_ARG
+
+
+def test_per_head_checks():
+    lib = _lib()
+    kv, seqs = _kv(), _seqs()
+    ph = _cfg(per_head=1)
+    assert _score(lib, kv, seqs, _cfg(per_head=2)) == sa.SA_ERR_INVALID_ARG
+    sals = _cfg(mode=sa.SA_MODE_SALS, unit_tokens=64, proj=FAKE, per_head=1)
+    assert _score(lib, kv, seqs, sals) == sa.SA_ERR_UNSUPPORTED      # per-head selection is Quest's
+    assert lib.sa_attn_heads_workspace_size(2, 32, 8, 32, 8) > lib.sa_attn_workspace_size(2, 32, 8, 32, 8)
+    assert lib.sa_attn_heads_workspace_size(2, 32, 8, 16385, 8) == 0  # the union supports 16384 pages
+    assert lib.sa_attn_heads_workspace_size(2, 32, 8, 32, 0) == 0
+    big = _seqs(max_pages=20000)
+    need = lib.sa_attn_heads_workspace_size(2, 32, 8, 32, 8)
+    call = lambda s, **kw: lib.sa_sparse_decode_attn_heads(
+        FAKE, sa.SA_BF16, 32, ctypes.byref(kv), ctypes.byref(s), kw.get("sel", FAKE), kw.get("num", FAKE),
+        kw.get("max_sel", 8), 0.088, FAKE, FAKE, kw.get("ws", need), None)
+    assert call(seqs, sel=None) == sa.SA_ERR_INVALID_ARG
+    assert call(seqs, max_sel=0) == sa.SA_ERR_INVALID_ARG
+    assert call(seqs, ws=need - 1) == sa.SA_ERR_WORKSPACE_TOO_SMALL
+    assert call(big) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sa_decode_step_workspace_size(32, ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(ph)) > \
+        lib.sa_decode_step_workspace_size(32, ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(_cfg()))
