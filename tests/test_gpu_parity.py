@@ -293,3 +293,34 @@ def test_attention_workspace_is_reusable():
         sa.sa_sparse_decode_attn(c.q(q), c.kv, c.seqs, sel, num, wl.softmax_scale, out, ws)
         ref = c.attention(sel, num, q)
         assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"call {i} differs"
+
+
+def _random_case(seed):
+    """A seeded random small workload: scoring mode, dtypes, group size, batch, ragged
+    lengths (down to a single token), budget and page-table layout."""
+    r = np.random.default_rng(1000 + seed)
+    mode = ["quest", "sals", "probe"][seed % 3]
+    hkv = int(r.choice([1, 2, 4]))
+    G = int(r.choice([1, 2, 4, 8]))
+    B = int(r.integers(1, 4))
+    lens = tuple(int(x) for x in r.integers(1, 5001, B))
+    kv = str(r.choice(["f32", "bf16"] if mode == "quest" else ["f32", "bf16", "i8"]))
+    qd = str(r.choice(["f32", "bf16"]))
+    kw = dict(B=B, Hq=hkv * G, Hkv=hkv, lens=lens, kv_dtype=kv, q_dtype=qd, mode=mode,
+              page_table=str(r.choice(["random", "contiguous"])))
+    if mode == "quest":
+        kw["budget_pages"] = int(r.integers(2, 40))
+    elif mode == "sals":
+        kw["k_compete"] = int(r.integers(0, 12))
+    else:
+        kw["unit_tokens"] = int(r.choice([16, 32, 64]))
+        kw["n_probe"] = int(r.integers(1, 13))
+        kw["k_compete"] = int(r.integers(0, 20))
+    return kw
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_random_workloads(seed):
+    kw = _random_case(seed)
+    wl = synth.make_custom(**kw, seed=500 + seed, name=f"random{seed}")
+    _full_check(wl, f"random{seed}: {kw}")

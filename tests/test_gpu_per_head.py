@@ -44,7 +44,20 @@ def _union_sizes(sel, num, G):
 
 @pytest.mark.parametrize("label", sorted(CASES))
 def test_per_head_step(label):
-    wl = synth.make_custom(**CASES[label], seed=21, name=label)
+    _check_per_head(synth.make_custom(**CASES[label], seed=21, name=label), label)
+
+
+@pytest.mark.parametrize("seed", range(4))
+def test_per_head_random(seed):
+    r = np.random.default_rng(2000 + seed)
+    hkv, G, B = int(r.choice([1, 2, 4])), int(r.choice([2, 4, 8, 16])), int(r.integers(1, 4))
+    kw = dict(B=B, Hq=hkv * G, Hkv=hkv, lens=tuple(int(x) for x in r.integers(1, 4001, B)),
+              kv_dtype=str(r.choice(["f32", "bf16"])), q_dtype=str(r.choice(["f32", "bf16"])),
+              budget_pages=int(r.integers(2, 48)), page_table=str(r.choice(["random", "contiguous"])))
+    _check_per_head(synth.make_custom(**kw, seed=600 + seed, name=f"ph_random{seed}"), f"ph_random{seed}: {kw}")
+
+
+def _check_per_head(wl, label):
     print(f"[gpu] per-head {label}: B={wl.B} Hq={wl.Hq} Hkv={wl.Hkv} lens={list(wl.seq_lens)} "
           f"kv={wl.kv_dtype} q={wl.q_dtype}", flush=True)
     c = GpuCase(wl)
