@@ -182,7 +182,8 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
             kv->num_pages <= kStepMaxPhysPages;
   // selection lists: one per kv-head, or one per query head with per_head
   const size_t lists = (size_t)s->batch * (L.per_head ? hq : kv->num_kv_heads);
-  L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel);
+  L.plan = plan_attention(s->batch, hq, kv->num_kv_heads, L.dense ? s->max_pages : L.max_sel,
+                          L.dense);
   L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
   const size_t fused_part = (size_t)L.splan.lists * L.splan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2);
   size_t off = 0;
@@ -360,7 +361,8 @@ int sa_sparse_decode_attn_heads(const void* q, int32_t q_dtype, int32_t num_q_he
 size_t sa_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t max_pages, int32_t max_sel) {
   if (batch < 1 || max_pages < 1 || !group_ok(num_q_heads, num_kv_heads)) return 0;
-  const AttnPlan p = plan_attention(batch, num_q_heads, num_kv_heads, max_sel > 0 ? max_sel : max_pages);
+  const AttnPlan p = plan_attention(batch, num_q_heads, num_kv_heads, max_sel > 0 ? max_sel : max_pages,
+                                    max_sel <= 0);
   return align_up(p.partial_floats * sizeof(float));
 }
 
@@ -376,7 +378,8 @@ int sa_sparse_decode_attn(const void* q, int32_t q_dtype, int32_t num_q_heads,
   if (sel && max_sel < 1) return SA_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
   const int list_len = sel ? max_sel : seqs->max_pages;
-  const AttnPlan plan = plan_attention(seqs->batch, num_q_heads, kv->num_kv_heads, list_len);
+  const AttnPlan plan = plan_attention(seqs->batch, num_q_heads, kv->num_kv_heads, list_len,
+                                       sel == nullptr);
   if (workspace_bytes < plan.partial_floats * sizeof(float)) return SA_ERR_WORKSPACE_TOO_SMALL;
   const Shapes s = shapes_of(num_q_heads, kv, seqs);
   return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale, kv->v_scale,

@@ -9,18 +9,107 @@ namespace {
 
 constexpr int kAttnThreads = 256;
 constexpr int kUnionMaxPages = kUnionPages;
+// split plan: about two workgroups per CU while a wave takes at most 16 pages,
+// else about eight (bandwidth-bound)
+constexpr long kLatencyWGs = 512, kBandwidthWGs = 2048, kMaxLatencyPPS = 64;
 
-// grid (nsplit, Hkv, B), block 256: one split of one (batch, kv-head) list
+// Device-side split plan of a dense pass over sequences of uneven length
+// ("SALS长序列推理优化", tiling algorithm for variable-length input: cut the
+// rows into basic blocks priced by a cost model, and bound every core by the
+// average cost).  The basic block is one page of one (b, kv-head) list, priced
+// by its bytes.  The pages over all lists fix the pages per split as the host
+// plan does for lists of one length (about two workgroups per CU while a wave
+// takes 16 pages or fewer, else about eight), and each list is cut into
+// max(1, ceil(pages / pps)) splits, so a short sequence no longer gets the
+// splits of the longest one.  Tasks are numbered b-major, then kv-head, then
+// split: the splits of a list are adjacent and so are its partial records.
+// Every workgroup of the attention and of the merge derives the same plan from
+// the lengths (one read of B words), so the plan needs no launch of its own and
+// no table in memory.  On return pre[b] is the first task of sequence b,
+// pre[B] the number of tasks and, if len_s is given, len_s[b] the clamped
+// length of sequence b.  NT threads, B <= kPlanMaxSeqs; all threads call.
+struct RaggedPlan {
+  int pps, tasks;
+};
+
+template <int NT>
+__device__ RaggedPlan ragged_plan(const int32_t* __restrict__ lens, int B, int max_pages, int hkv,
+                                  int* pre, uint32_t* red, int* len_s = nullptr) {
+  constexpr int NW = NT / 64, PER = kPlanMaxSeqs / NT;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int pg[PER];
+  uint32_t sum = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {  // thread tid holds sequences PER * tid .. + PER - 1
+    const int b = PER * tid + e;
+    const int L = b < B ? clamp_len(lens[b], max_pages) : 0;
+    if (len_s && b < B) len_s[b] = L;
+    pg[e] = (L + kPage - 1) / kPage;
+    sum += (uint32_t)pg[e];
+  }
+  uint32_t incl = wave_incl_scan_u32(sum);
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  uint64_t total = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) total += red[w];
+  total *= (uint64_t)hkv;  // pages over all lists
+  uint64_t pps = ((total + kLatencyWGs - 1) / kLatencyWGs + 3) / 4 * 4;
+  if (pps > kMaxLatencyPPS) pps = (total + kBandwidthWGs - 1) / kBandwidthWGs;
+  if (pps < 4) pps = 4;
+  uint32_t cnt = 0, sp[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int b = PER * tid + e;
+    sp[e] = b < B ? (uint32_t)hkv * (uint32_t)max(1, (int)((pg[e] + pps - 1) / pps)) : 0u;
+    cnt += sp[e];
+  }
+  incl = wave_incl_scan_u32(cnt);
+  __syncthreads();  // every wave has read red
+  if (lane == 63) red[wave] = incl;
+  __syncthreads();
+  uint32_t off = incl - cnt, tasks = 0;
+#pragma unroll
+  for (int w = 0; w < NW; ++w) {
+    if (w < wave) off += red[w];
+    tasks += red[w];
+  }
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int b = PER * tid + e;
+    if (b < B) pre[b] = (int)off;
+    off += sp[e];
+  }
+  if (tid == 0) pre[B] = (int)tasks;
+  __syncthreads();
+  return {(int)pps, (int)tasks};
+}
+
+// The sequence, kv-head and split of planned task t (< pre[B]).
+__device__ __forceinline__ void ragged_task(const int* pre, int B, int hkv, int t, int& b, int& h,
+                                            int& split) {
+  int lo = 0, hi = B - 1;  // the last sequence whose first task is <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) >> 1;
+    if (pre[mid] <= t) lo = mid;
+    else hi = mid - 1;
+  }
+  b = lo;
+  const int spl = (pre[b + 1] - pre[b]) / hkv, r = t - pre[b];
+  h = r / spl;
+  split = r % spl;
+}
+
+// One split of one (batch, kv-head) list: pages [split * pps, + pps) of the
+// sequence (sel == nullptr) or of its selected list, into the partial records
+// part[G][kPartStride].
 template <int KT, int QT, int G>
-__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
+__device__ __forceinline__ void attn_task(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs, int num_pages, int hkv,
-    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
-    const int32_t* __restrict__ sel, const int32_t* __restrict__ num_sel, int max_sel, int pps,
-    int nsplit, float scale_log2, float* __restrict__ partials, int masked) {
-  __shared__ AttnSmem<G> sm;
-  const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const int L = clamp_len(lens[b], max_pages);
+    const int32_t* __restrict__ pt, int max_pages, const int32_t* __restrict__ sel,
+    const int32_t* __restrict__ num_sel, int max_sel, int b, int h, int split, int pps, int L,
+    float scale_log2, float* __restrict__ part, int masked, AttnSmem<G>& sm) {
   int cnt = (L + kPage - 1) / kPage;
   const int32_t* lst = nullptr;
   if (sel) {
@@ -30,7 +119,6 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   const int j0 = split * pps, j1 = min(j0 + pps, cnt);
   // the split's list entries are read together with the list length
   const int jcap = sel ? min(j0 + pps, max_sel) : -1;
-  float* part = partials + (((size_t)b * hkv + h) * nsplit + split) * G * kPartStride;
   // four or more bf16 query heads per kv-head: scores on the matrix cores
   if constexpr (G >= 4 && QT == SA_BF16 && (KT == SA_BF16 || KT == SA_I8))
     attend_range_mfma<KT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
@@ -38,6 +126,40 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
   else
     attend_range<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
                             lst, j0, j1, scale_log2, part, sm, nullptr, jcap, masked != 0);
+}
+
+// grid (nsplit, Hkv, B), block 256: one split of one (batch, kv-head) list.
+// PLAN (dense passes only): grid (bound on the tasks), task blockIdx.x of the
+// device plan above; workgroups past the plan's tasks return at once.  (Dealing
+// the tasks round-robin over a grid of resident workgroups, so that each pays
+// for the plan once, measured slower: the hardware's dynamic dispatch of
+// one-task workgroups balances uneven workgroup times better.)
+template <int KT, int QT, int G, bool PLAN>
+__global__ __launch_bounds__(kAttnThreads) void attn_kernel(
+    const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
+    const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs, int num_pages, int hkv,
+    const int32_t* __restrict__ pt, const int32_t* __restrict__ lens, int max_pages,
+    const int32_t* __restrict__ sel, const int32_t* __restrict__ num_sel, int max_sel, int pps,
+    int nsplit, float scale_log2, float* __restrict__ partials, int masked, int B) {
+  __shared__ AttnSmem<G> sm;
+  if constexpr (PLAN) {
+    __shared__ int pre[kPlanMaxSeqs + 1], len_s[kPlanMaxSeqs];
+    __shared__ uint32_t red[kAttnThreads / 64];
+    const RaggedPlan rp = ragged_plan<kAttnThreads>(lens, B, max_pages, hkv, pre, red, len_s);
+    const int t = blockIdx.x;
+    if (t >= rp.tasks) return;
+    int b, h, split;
+    ragged_task(pre, B, hkv, t, b, h, split);
+    attn_task<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, pt, max_pages, sel, num_sel, max_sel, b, h,
+                         split, rp.pps, len_s[b], scale_log2,
+                         partials + (size_t)t * G * kPartStride, masked, sm);
+  } else {
+    const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
+    attn_task<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, pt, max_pages, sel, num_sel, max_sel, b, h,
+                         split, pps, clamp_len(lens[b], max_pages), scale_log2,
+                         partials + (((size_t)b * hkv + h) * nsplit + split) * G * kPartStride,
+                         masked, sm);
+  }
 }
 
 // grid (Hkv, B), block 256: the union of the page lists of the G query heads
@@ -89,27 +211,39 @@ __global__ __launch_bounds__(kAttnThreads) void union_kernel(
 }
 
 // grid (G, Hkv, B), block 256: merge the splits of one query head of one list
-// (two thread groups of 128 outputs, each folding half of the splits)
+// (two thread groups of 128 outputs, each folding half of the splits).  PLAN:
+// the list's splits and records come from the device plan of the attention.
+template <bool PLAN>
 __global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __restrict__ partials,
                                                             int hkv, int G, int nsplit,
-                                                            float* __restrict__ out) {
+                                                            float* __restrict__ out,
+                                                            const int32_t* __restrict__ lens, int B,
+                                                            int max_pages) {
   __shared__ float lds[3 * kAttnThreads];
   const int g = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
-  const size_t list = (size_t)b * hkv + h;
-  merge_list(partials + list * nsplit * G * kPartStride, nsplit, G,
+  size_t first = ((size_t)b * hkv + h) * nsplit;
+  int ns = nsplit;
+  if constexpr (PLAN) {
+    __shared__ int pre[kPlanMaxSeqs + 1];
+    __shared__ uint32_t red[kAttnThreads / 64];
+    ragged_plan<kAttnThreads>(lens, B, max_pages, hkv, pre, red);
+    ns = (pre[b + 1] - pre[b]) / hkv;
+    first = (size_t)pre[b] + (size_t)h * ns;
+  }
+  merge_list(partials + first * G * kPartStride, ns, G,
              out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, lds, nullptr, g, 1);
 }
 
-template <int KT, int QT>
+template <int KT, int QT, bool PLAN>
 hipError_t attn_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, const void* k,
                            const void* v, const uint16_t* ks, const uint16_t* vs, const Shapes& s,
                            const int32_t* pt, const int32_t* lens, const int32_t* sel,
                            const int32_t* num_sel, int max_sel, const AttnPlan& plan,
                            float scale_log2, float* partials, int masked) {
 #define SA_AT(GG)                                                                               \
-  hipLaunchKernelGGL((attn_kernel<KT, QT, GG>), grid, dim3(kAttnThreads), 0, st, q, k, v, ks,   \
-                     vs, s.num_pages, s.Hkv, pt, lens, s.max_pages, sel, num_sel, max_sel,      \
-                     plan.pps, plan.nsplit, scale_log2, partials, masked)
+  hipLaunchKernelGGL((attn_kernel<KT, QT, GG, PLAN>), grid, dim3(kAttnThreads), 0, st, q, k, v, \
+                     ks, vs, s.num_pages, s.Hkv, pt, lens, s.max_pages, sel, num_sel, max_sel,  \
+                     plan.pps, plan.nsplit, scale_log2, partials, masked, s.B)
   switch (G) {
     case 1: SA_AT(1); break;
     case 2: SA_AT(2); break;
@@ -123,14 +257,13 @@ hipError_t attn_dispatch_g(int G, dim3 grid, hipStream_t st, const void* q, cons
 
 }  // namespace
 
-AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len) {
+AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len, bool dense) {
   // Selected lists: about two workgroups per CU, each wave taking the same
   // whole number of pages.  Measured on the GQA, SALS and large workloads,
   // fewer and longer splits beat filling the CUs: every split pays the list,
   // page-table and query round trips once, and the merge reads one record per
   // split.  Past 16 pages per wave the pass is bound by bandwidth, and more
   // workgroups (about eight per CU) keep more bytes in flight.
-  constexpr long kLatencyWGs = 512, kBandwidthWGs = 2048, kMaxLatencyPPS = 64;
   AttnPlan p{};
   p.list_len = list_len < 1 ? 1 : list_len;
   const long lists = (long)B * Hkv;
@@ -142,6 +275,16 @@ AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len) {
   p.pps = (int)pps;
   p.nsplit = (p.list_len + p.pps - 1) / p.pps;
   p.partial_floats = (size_t)lists * p.nsplit * G * kPartStride;
+  p.tasks = 0;
+  // a batch of one sequence has nothing to balance: the host plan is the same
+  if (dense && B > 1 && B <= kPlanMaxSeqs) {
+    // the device plan cuts the pages actually present: fewer than
+    // min(kBandwidthWGs, pages / 4) + one per list tasks (see ragged_plan)
+    const long bound = (pages / 4 < kBandwidthWGs ? pages / 4 : kBandwidthWGs) + lists + 1;
+    p.tasks = (int)bound;
+    const size_t pf = (size_t)bound * G * kPartStride;
+    if (pf > p.partial_floats) p.partial_floats = pf;
+  }
   return p;
 }
 
@@ -153,11 +296,16 @@ hipError_t launch_attention(int kv_dtype, int q_dtype, const void* q, const void
                             float* out, hipStream_t st, bool masked) {
   const int G = s.Hq / s.Hkv;
   const float sl2 = softmax_scale * kLog2e;
-  dim3 grid(plan.nsplit, s.Hkv, s.B);
+  const bool planned = sel == nullptr && plan.tasks > 0 && s.B <= kPlanMaxSeqs;
+  const dim3 grid = planned ? dim3(plan.tasks) : dim3(plan.nsplit, s.Hkv, s.B);
   hipError_t e;
-#define SA_KQ(KT, QT)                                                                        \
-  e = attn_dispatch_g<KT, QT>(G, grid, st, q, k, v, k_scale, v_scale, s, pt, lens, sel, num_sel, \
-                              max_sel, plan, sl2, partials, masked ? 1 : 0)
+#define SA_KQ(KT, QT)                                                                          \
+  e = planned ? attn_dispatch_g<KT, QT, true>(G, grid, st, q, k, v, k_scale, v_scale, s, pt, lens, \
+                                              sel, num_sel, max_sel, plan, sl2, partials,        \
+                                              masked ? 1 : 0)                                    \
+              : attn_dispatch_g<KT, QT, false>(G, grid, st, q, k, v, k_scale, v_scale, s, pt,    \
+                                               lens, sel, num_sel, max_sel, plan, sl2, partials, \
+                                               masked ? 1 : 0)
   if (kv_dtype == SA_F32) {
     if (q_dtype == SA_F32) SA_KQ(SA_F32, SA_F32); else SA_KQ(SA_F32, SA_BF16);
   } else if (kv_dtype == SA_BF16) {
@@ -167,8 +315,12 @@ hipError_t launch_attention(int kv_dtype, int q_dtype, const void* q, const void
   }
 #undef SA_KQ
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(merge_kernel, dim3(G, s.Hkv, s.B), dim3(kAttnThreads), 0, st, partials, s.Hkv,
-                     G, plan.nsplit, out);
+  if (planned)
+    hipLaunchKernelGGL(merge_kernel<true>, dim3(G, s.Hkv, s.B), dim3(kAttnThreads), 0, st, partials,
+                       s.Hkv, G, plan.nsplit, out, lens, s.B, s.max_pages);
+  else
+    hipLaunchKernelGGL(merge_kernel<false>, dim3(G, s.Hkv, s.B), dim3(kAttnThreads), 0, st, partials,
+                       s.Hkv, G, plan.nsplit, out, lens, s.B, s.max_pages);
   return hipGetLastError();
 }
 

@@ -209,9 +209,13 @@ struct AttnPlan {
   int list_len;   // pages per (b, kv-head) list the kernel may visit
   int pps;        // pages per split
   int nsplit;     // splits per list
+  int tasks;      // dense passes: workgroups of the device-planned launch (0: the host plan)
   size_t partial_floats;  // workspace floats
 };
-AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len);
+constexpr int kPlanMaxSeqs = 1024;  // sequences of a device-planned dense pass
+// dense: a pass over every page of each sequence, split by the device plan
+// from the actual lengths (B <= kPlanMaxSeqs)
+AttnPlan plan_attention(int B, int Hq, int Hkv, int list_len, bool dense = false);
 
 // Per-head selection: the union of a group's per-head page lists (ascending,
 // (head mask << 16) | page entries, umax per list) for the masked attention.

@@ -148,6 +148,33 @@ def test_dense_attention_matches_oracle(kv_dtype):
     check_attention(wl, g, o, what="dense attention")
 
 
+@pytest.mark.parametrize("shape", ["many_uneven", "one_long", "past_plan_limit"])
+def test_dense_ragged_batches(shape):
+    """Dense passes over batches of very uneven lengths (empty sequences included):
+    the device split plan cuts each list by its own length.  past_plan_limit has
+    more sequences than the device plan takes, so the host plan runs instead."""
+    rng = np.random.default_rng({"many_uneven": 31, "one_long": 32, "past_plan_limit": 33}[shape])
+    if shape == "many_uneven":
+        lens = rng.choice([0, 1, 15, 16, 17, 100, 555, 2000, 6000], size=300)
+        kw = dict(Hq=8, Hkv=2, kv_dtype="bf16")
+    elif shape == "one_long":
+        lens = np.array([65536, 1, 0, 33, 16])
+        kw = dict(Hq=16, Hkv=8, kv_dtype="i8", mode="sals")
+    else:
+        lens = rng.integers(0, 48, size=1100)
+        kw = dict(Hq=4, Hkv=4, kv_dtype="f32")
+    wl = synth.make_custom(B=len(lens), lens=tuple(int(x) for x in lens), q_dtype="bf16",
+                           page_table="random", seed=34, **kw)
+    print(f"[gpu] dense ragged {shape}: B={wl.B} pages={sum(wl.n_pages(b) for b in range(wl.B))}",
+          flush=True)
+    c = GpuCase(wl)
+    g = c.attention(None, None).cpu().numpy()
+    o = oracle.attention(wl.q, wl.q_dtype, wl.k, wl.v, wl.kv_dtype, wl.k_scale, wl.v_scale,
+                         wl.page_table, wl.seq_lens, None, None, wl.softmax_scale)
+    check_attention(wl, g, o, what=f"dense ragged {shape}")
+    assert np.all(g[np.asarray(lens) == 0] == 0.0), "an empty sequence attends to nothing"
+
+
 def test_all_pages_budget_equals_dense():
     """Budget >= every unit: the step skips scoring and equals dense attention."""
     wl = synth.make_custom(B=2, Hq=16, Hkv=4, lens=(3000, 2000), kv_dtype="bf16", q_dtype="bf16",
