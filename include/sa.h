@@ -259,7 +259,11 @@ size_t sa_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv
  * int8 caches use k = code * k_scale and v = code * v_scale.
  * sel: [batch, num_kv_heads, max_sel] logical pages (from sa_topk_pages), with
  * num_sel [batch, num_kv_heads] valid entries; sel == NULL and num_sel == NULL
- * selects every page of every sequence (dense decode attention).
+ * selects every page of every sequence (dense decode attention).  A dense
+ * pass over 2 .. 1024 sequences sizes its splits on the device from the
+ * actual lengths, so short sequences get few splits [SALS tiling for
+ * variable-length input]; the result does not depend on the split plan
+ * beyond fp32 rounding order.
  * out: [batch, num_q_heads, head_dim] fp32.  A sequence with no valid token
  * gets zeros.  workspace: >= sa_attn_workspace_size(...) bytes.
  */
