@@ -303,6 +303,36 @@ def test_step_graph_replays_match_eager(gqa):
         c.step()  # eager work between replays
 
 
+def test_dense_ragged_graph_replays_match_eager():
+    """The device-planned dense pass captured in a HIP graph: every replay, with eager
+    work and new sequence lengths between replays, equals the eager call on the same
+    lengths bit for bit (the plan is read from the lengths at run time)."""
+    wl = synth.make_custom(B=5, Hq=8, Hkv=2, lens=(4000, 0, 17, 2500, 900), kv_dtype="bf16",
+                           q_dtype="bf16", page_table="random", seed=35)
+    print("[gpu] dense ragged graph replay", flush=True)
+    c = GpuCase(wl)
+    ws = sa.alloc_workspace(sa.sa_attn_workspace_size(wl.B, wl.Hq, wl.Hkv, wl.max_pages, 0), c.dev)
+    out = torch.zeros((wl.B, wl.Hq, wl.d), dtype=torch.float32, device=c.dev)
+    lens_t = c.d.seq_lens
+    lens0 = lens_t.clone()
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        with torch.cuda.graph(g, stream=s):
+            sa.sa_sparse_decode_attn(c.d.q, c.kv, c.seqs, None, None, wl.softmax_scale, out, ws)
+    torch.cuda.current_stream().wait_stream(s)
+    variants = [lens0, torch.tensor([3, 4000, 0, 16, 2500], dtype=torch.int32, device=c.dev), lens0]
+    for rep, lv in enumerate(variants):
+        lens_t.copy_(lv)
+        ref = c.attention(None, None)  # eager, same lengths
+        out.fill_(float("nan"))
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out.view(torch.int32), ref.view(torch.int32)), f"replay {rep}"
+    lens_t.copy_(lens0)
+
+
 def test_attention_workspace_is_reusable():
     """Three split-K attention calls on one workspace, each with a new query, equal
     calls on fresh workspaces bit for bit (no state is carried between calls)."""
