@@ -392,17 +392,21 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
   }
 }
 
-constexpr int kProbeUnitsPerWG = 4;  // one block per wave
+constexpr int kProbeUnitsPerWave = 4;
+constexpr int kProbeUnitsPerWG = 4 * kProbeUnitsPerWave;
 
 // Probe sampling [RK, the probe signal of the block selector]: the score of
 // block u is the largest q_g . k_t over its probed positions t (step =
 // max(1, len / n_probe) from the block start) and the group's query heads g.
-// grid (ceil(max_units / 4), Hkv, B), block 256: the group's query rows are
-// staged in LDS as fp32; wave w takes block blockIdx.x * 4 + w.  Lanes are
-// (probe slot of 8, dimension group of 8 x 16): each round reads up to eight
-// probed key rows (16 dimensions per lane), sums each slot's partial dots over
-// its eight lanes by DPP, and keeps the maximum; the eight slots are merged by
-// a row maximum and two lane swaps.  int8 keys: the dot of the codes times the
+// grid (ceil(max_units / 16), Hkv, B), block 256: the group's query rows are
+// staged in LDS as fp32; wave w takes the four consecutive blocks from
+// (blockIdx.x * 4 + w) * 4, with the page-table entries and then the key rows
+// of all four in flight together (one block per wave left each wave a chain of
+// dependent round trips for 2 KB of keys).  Lanes are (probe slot of 8,
+// dimension group of 8 x 16): each round reads up to eight probed key rows per
+// block (16 dimensions per lane), sums each slot's partial dots over its eight
+// lanes by DPP, and keeps the maximum; the eight slots are merged by a row
+// maximum and two lane swaps.  int8 keys: the dot of the codes times the
 // token's scale.
 template <int KT, int QT, int G>
 __global__ __launch_bounds__(256) void probe_score_kernel(
@@ -410,6 +414,7 @@ __global__ __launch_bounds__(256) void probe_score_kernel(
     const uint16_t* __restrict__ k_scale, int num_pages, int hkv, const int32_t* __restrict__ pt,
     const int32_t* __restrict__ lens, int max_pages, int unit_tokens, int n_probe,
     float* __restrict__ scores, int max_units) {
+  constexpr int UPW = kProbeUnitsPerWave;
   __shared__ float qs[G][kHeadDim];
   const int h = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -421,46 +426,73 @@ __global__ __launch_bounds__(256) void probe_score_kernel(
   __syncthreads();
   const int L = clamp_len(lens[b], max_pages);
   const int nu = (L + unit_tokens - 1) / unit_tokens;
-  const int u = blockIdx.x * kProbeUnitsPerWG + wave;
-  if (u >= nu) return;  // wave-uniform, and no barrier follows
-  const int t0 = u * unit_tokens, t1 = min(t0 + unit_tokens, L);
-  const int step = max(1, (t1 - t0) / n_probe);
-  const int ns = (t1 - t0 + step - 1) / step;  // probed positions
+  const int ub = (blockIdx.x * 4 + wave) * UPW;
+  if (ub >= nu) return;  // wave-uniform, and no barrier follows
+  int t0[UPW], stp[UPW], ns[UPW];
+  int ns_max = 0;
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const int u = ub + j;
+    t0[j] = 0;
+    stp[j] = 1;
+    ns[j] = 0;  // blocks past the sequence probe nothing
+    if (u < nu) {
+      t0[j] = u * unit_tokens;
+      const int t1 = min(t0[j] + unit_tokens, L);
+      stp[j] = max(1, (t1 - t0[j]) / n_probe);
+      ns[j] = (t1 - t0[j] + stp[j] - 1) / stp[j];
+    }
+    ns_max = max(ns_max, ns[j]);
+  }
   const int slot = lane >> 3, dg = lane & 7;
   const int32_t* pt_row = pt + (size_t)b * max_pages;
-  float best = -INFINITY;
-  for (int i0 = 0; i0 < ns; i0 += 8) {
+  float best[UPW];
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) best[j] = -INFINITY;
+  for (int i0 = 0; i0 < ns_max; i0 += 8) {
     const int i = i0 + slot;
-    const bool valid = i < ns;
-    const int t = t0 + (valid ? i : 0) * step;
-    const int pp = pt_row[t >> 4];
-    const bool ok = valid && pp >= 0 && pp < num_pages;
-    const size_t row = ((size_t)(ok ? pp : 0) * kPage + (t & 15)) * hkv + h;
-    float x[16];
-    {
+    int pp[UPW], t[UPW];
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+      t[j] = t0[j] + (i < ns[j] ? i : 0) * stp[j];
+      pp[j] = pt_row[t[j] >> 4];
+    }
+    bool ok[UPW];
+    float x[UPW][16], sc[UPW];
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+      ok[j] = i < ns[j] && pp[j] >= 0 && pp[j] < num_pages;
+      const size_t row = ((size_t)(ok[j] ? pp[j] : 0) * kPage + (t[j] & 15)) * hkv + h;
       float a[8], c[8];
       load8<KT>(k, row * kHeadDim + 16 * dg, a);
       load8<KT>(k, row * kHeadDim + 16 * dg + 8, c);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        x[e] = a[e];
-        x[8 + e] = c[e];
+        x[j][e] = a[e];
+        x[j][8 + e] = c[e];
+      }
+      sc[j] = KT == SA_I8 ? f16_to_f32(k_scale[row]) : 1.0f;
+    }
+    constexpr int GU = G > 4 ? 2 : G;  // larger groups: query rows re-read from LDS, not held
+#pragma unroll
+    for (int j = 0; j < UPW; ++j) {
+#pragma unroll GU
+      for (int g = 0; g < G; ++g) {
+        float dot = 0.0f;
+#pragma unroll
+        for (int e = 0; e < 16; ++e) dot = fmaf(qs[g][16 * dg + e], x[j][e], dot);
+        dot += dpp_f32<kDppXor1>(dot);
+        dot += dpp_f32<kDppXor2>(dot);
+        dot += dpp_f32<kDppHalfMirror>(dot);
+        if (ok[j]) best[j] = fmaxf(best[j], dot * sc[j]);
       }
     }
-    const float sc = KT == SA_I8 ? f16_to_f32(k_scale[row]) : 1.0f;
-#pragma unroll
-    for (int g = 0; g < G; ++g) {
-      float dot = 0.0f;
-#pragma unroll
-      for (int e = 0; e < 16; ++e) dot = fmaf(qs[g][16 * dg + e], x[e], dot);
-      dot += dpp_f32<kDppXor1>(dot);
-      dot += dpp_f32<kDppXor2>(dot);
-      dot += dpp_f32<kDppHalfMirror>(dot);
-      if (ok) best = fmaxf(best, dot * sc);
-    }
   }
-  best = pair32_max(pair16_max(max16(best)));
-  if (lane == 0) scores[((size_t)b * hkv + h) * max_units + u] = best;
+#pragma unroll
+  for (int j = 0; j < UPW; ++j) {
+    const float bj = pair32_max(pair16_max(max16(best[j])));
+    if (lane == 0 && ub + j < nu) scores[((size_t)b * hkv + h) * max_units + ub + j] = bj;
+  }
 }
 
 template <int KT, int QT, bool PH>
