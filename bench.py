@@ -260,6 +260,7 @@ def main():
                                                         None, wl.softmax_scale, out, dws),
                      max(20, args.steps // 4))
     dense_bytes = synth.dense_bytes(wl)
+    stream_gbs = stream_read_gbs(dev, stream)
     # the step is one persistent kernel (score -> top-K -> attention -> merge), so it is the
     # dominant kernel; its launch duration is the graph's per-step time
     dom_name = "quest_step_kernel (fused decode step)"
@@ -293,6 +294,8 @@ def main():
         "eager_step_us_p10_p50_p90": [round(float(np.percentile(per, p)), 2) for p in (10, 50, 90)],
         "step_bytes": nb["total"],
         "hbm_peak_frac": round(step_gbs / PEAK_GBS, 4),
+        "stream_read_gbs": round(stream_gbs, 1),
+        "stream_read_frac": round(step_gbs / stream_gbs, 4),
         "dense_us": round(dense_us, 2),
         "dense_gbs": round(dense_bytes / (dense_us * 1e-6) / 1e9, 1),
         "speedup_vs_dense": round(dense_us / (ms_per_step * 1e3), 2),
@@ -309,6 +312,33 @@ def main():
 
 
 CONFIG_COPIES_BYTES = 4 << 30  # layer copies rotated: at least this many bytes of K/V in all
+STREAM_BYTES = 4 << 30         # streaming-read probe: 16x the 256 MB Infinity Cache
+
+
+def stream_read_gbs(dev, stream, reps=8):
+    """GB/s of one plain streaming read of STREAM_BYTES (sa_stream_read), the best of reps
+    timed launches: the bandwidth a pure HBM read reaches on this device."""
+    import torch
+
+    import query_aware_sparse_min_amd as sa
+
+    src = torch.ones(STREAM_BYTES // 4, dtype=torch.float32, device=dev)
+    sink = torch.zeros(1 << 14, dtype=torch.int32, device=dev)
+    for _ in range(2):
+        sa.sa_stream_read(src, sink)
+    torch.cuda.synchronize()
+    best = None
+    for _ in range(reps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        sa.sa_stream_read(src, sink)
+        b.record(stream)
+        torch.cuda.synchronize()
+        ms = a.elapsed_time(b)
+        best = ms if best is None else min(best, ms)
+    del src, sink
+    torch.cuda.empty_cache()
+    return STREAM_BYTES / (best * 1e-3) / 1e9
 
 
 def config_line(name, args):
@@ -562,23 +592,55 @@ def append_line(name, args):
     torch.cuda.empty_cache()
 
 
+def host_description():
+    """Host cores and CPU model of the machine the oracle runs on."""
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    model = ln.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    affinity = len(os.sched_getaffinity(0)) if hasattr(os, "sched_getaffinity") else os.cpu_count()
+    return {"nproc": os.cpu_count(), "cores_available": affinity, "cpu_model": model}
+
+
 def cpu_baseline(wl, seconds, step_bytes):
-    """The oracle's decode step on the host, on as many fresh queries as fit in ~seconds."""
+    """The oracle's decode step on the host, on fresh queries for about `seconds` per leg:
+    single-threaded, then with its OpenMP outer loops (one (b, kv-head) list or query head per
+    iteration) over the cores the process may use (OMP_NUM_THREADS caps them)."""
     import oracle
     import synth
 
+    host = host_description()
+    omp = int(os.environ.get("OMP_NUM_THREADS", "0") or 0) or host["cores_available"]
+    omp = max(1, min(omp, host["cores_available"]))
     meta, _ = oracle.build_meta(wl)  # amortised, like the GPU's metadata build
-    n, t_used = 0, 0.0
-    while n < 400 and (t_used < seconds or n == 0):
-        q = synth.fresh_q(wl, n)
-        t = time.perf_counter()
-        oracle.decode_step(wl, meta, None, q=q)
-        t_used += time.perf_counter() - t
-        n += 1
-    per_step = t_used / n
-    return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": 1,
-            "kind": "oracle", "step_ms": round(per_step * 1e3, 1),
-            "sample": f"{n} full decode steps of the same workload (all 32 heads), fresh query each"}
+
+    def leg(threads, first_q):
+        oracle.set_threads(threads)
+        n, t_used = 0, 0.0
+        while n < 400 and (t_used < seconds or n == 0):
+            q = synth.fresh_q(wl, first_q + n)
+            t = time.perf_counter()
+            oracle.decode_step(wl, meta, None, q=q)
+            t_used += time.perf_counter() - t
+            n += 1
+        oracle.set_threads(1)
+        per_step = t_used / n
+        return {"value": round(step_bytes / per_step / 1e9, 4), "unit": "GB/s", "cores": threads,
+                "step_ms": round(per_step * 1e3, 2), "steps": n}
+
+    one = leg(1, 0)
+    many = leg(omp, 1000)
+    return {**many, "kind": "oracle",
+            "sample": (f"{many['steps']} full decode steps of the same workload (all {wl.Hkv} lists), "
+                       f"fresh query each, OpenMP over the lists on {omp} threads; a single-threaded "
+                       f"leg of {one['steps']} steps is under single_thread"),
+            "label": "plain double-precision oracle (not a tuned CPU implementation)",
+            "single_thread": one, "host": host}
 
 
 if __name__ == "__main__":

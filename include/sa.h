@@ -40,7 +40,10 @@
  *  - Errors are returned as negative sa_status codes; nothing aborts or
  *    throws across this interface.
  *  - Thread safety: calls on distinct streams (or with distinct buffers) are
- *    independent; the library keeps no mutable global state.
+ *    independent.  The only library-wide state is a per-device cache of
+ *    fixed device and kernel properties (compute-unit count, the fused step
+ *    kernel's resident workgroups), filled on first use with atomic stores;
+ *    it never changes what a call computes.
  *  - Sequence semantics: seq_lens[b] >= 1 counts the current token, whose K/V
  *    is already in the cache; attention covers positions [0, seq_lens[b]).
  *    Sequence b has n_b = ceil(seq_lens[b] / 16) logical pages; page_table
@@ -222,10 +225,6 @@ int sa_topk_pages(const float *scores, int32_t num_kv_heads, const sa_seqs *seqs
                   const sa_select_cfg *cfg, int32_t *sel, int32_t *num_sel, void *stream);
 
 /*
- * Workspace of sa_sparse_decode_attn for lists of up to max_sel pages
- * (max_sel <= 0: dense mode over max_pages pages).  0 on bad input.
- */
-/*
  * sa_sparse_decode_attn_heads - attention with per-head selection [Quest, GQA
  * section: each query head's own pages, and the union the group then reads].
  * sel: [batch, num_q_heads, max_sel] logical pages, one list per query head
@@ -246,6 +245,15 @@ int sa_sparse_decode_attn_heads(const void *q, int32_t q_dtype, int32_t num_q_he
 size_t sa_attn_heads_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                                     int32_t max_pages, int32_t max_sel);
 
+/*
+ * Workspace bytes of sa_sparse_decode_attn for a batch of `batch` sequences
+ * with num_q_heads / num_kv_heads heads, page-table rows of max_pages entries
+ * and selection lists of up to max_sel pages (max_sel <= 0: a dense pass over
+ * up to max_pages pages per sequence).  The workspace holds the split-K
+ * partial records (max, sum and accumulator per split and query head); it
+ * needs no initial contents.  0 on bad input (unsupported group size,
+ * batch < 1, max_pages < 1).
+ */
 size_t sa_attn_workspace_size(int32_t batch, int32_t num_q_heads, int32_t num_kv_heads,
                               int32_t max_pages, int32_t max_sel);
 
@@ -287,18 +295,43 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  * the step runs sa_score_pages -> sa_topk_pages over the query heads ->
  * sa_sparse_decode_attn_heads, and sel / num_sel are per query head:
  * [batch, num_q_heads, sa_max_selected] and [batch, num_q_heads].
- * Quest mode with one query head per kv-head runs as a single persistent
- * kernel whose workgroups hand work to each other through the workspace
- * (an error word, score keys and partial records, where 0 means "not written
- * yet"): the workspace must be zero-filled before its first use, every call
- * leaves those words zero again, and one workspace serves one call at a time.
- * A bounded wait that times out (never expected) sets the 32-bit word at byte
- * offset 8 of the workspace to nonzero.
+ * Quest mode with one query head per kv-head and lists of up to 4096 pages
+ * runs as a single persistent kernel (one workgroup per compute unit) whose
+ * workgroups hand score keys and partial records to each other through the
+ * workspace; no workgroup ever waits for another, so the result does not
+ * depend on how many of them are resident at a time (a build that uses
+ * scratch memory runs the separate kernels instead; same results).
+ * Workspace protocol of every sa_decode_step call:
+ *  - the workspace must be zero-filled before its first use;
+ *  - every call leaves its hand-off words (per-list arrival counters and score
+ *    keys) zero again when it completes; a call that does not complete (the
+ *    process or the device is stopped mid-kernel) leaves them undefined, and
+ *    the workspace must then be zero-filled before it is used again;
+ *  - one workspace serves one call at a time: calls that share it must be
+ *    ordered on one stream.
+ * The environment variable SA_STEP_MAX_WORKGROUPS (a positive integer, read
+ * at every call) caps the persistent kernel's workgroups, e.g. to leave
+ * compute units to other work; the result is the same bit for bit.
  */
 int sa_decode_step(const void *q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache *kv,
                    const sa_seqs *seqs, const sa_select_cfg *cfg, const void *meta,
                    const uint16_t *meta_scale, float softmax_scale, float *out, int32_t *sel,
                    int32_t *num_sel, void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * sa_stream_read - measurement helper, not a step of the path: reads `bytes`
+ * (a nonzero multiple of 16) of device memory at src (16-byte aligned) once,
+ * with 16-byte loads spread over about eight workgroups per compute unit, so
+ * that its time gives the bandwidth a plain streaming read reaches on this
+ * device.  The decode step is bound by the bytes it reads ([SeqO1] bottleneck
+ * analysis; [Quest] read-volume formula), so this is the second denominator
+ * its effective bandwidth is quoted against, beside the HBM peak.  sink:
+ * device words, one per workgroup (min(sink_words, 8 * compute units)
+ * workgroups); they are written only when a workgroup's XOR of its words
+ * equals one fixed value.  SA_ERR_INVALID_ARG on a null or misaligned src,
+ * a bad size, or a null sink.
+ */
+int sa_stream_read(const void *src, size_t bytes, uint32_t *sink, size_t sink_words, void *stream);
 
 #ifdef __cplusplus
 }

@@ -31,8 +31,8 @@ PAGE = 16
 def build(verbose: bool = False) -> str:
     src = os.path.join(_HERE, "sa_oracle.c")
     tmp = _LIB_PATH + ".tmp"
-    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-ffp-contract=off", "-fno-fast-math",
-           "-Wall", "-o", tmp, src, "-lm"]
+    cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
+           "-fno-fast-math", "-Wall", "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
@@ -65,8 +65,17 @@ def _load():
     lib.oracle_attention.argtypes = [vp, i, i, vp, vp, i, vp, vp, i, i, i, vp, vp, i, i, vp, vp, i,
                                      d, vp, i, vp]
     lib.oracle_attention.restype = None
+    lib.oracle_set_threads.argtypes = [i]
+    lib.oracle_set_threads.restype = None
+    lib.oracle_set_threads(1)  # single-threaded unless set_threads() says otherwise
     _lib = lib
     return lib
+
+
+def set_threads(n: int) -> None:
+    """Host threads of the oracle's outer loops (independent outputs; results do not depend
+    on the count)."""
+    _load().oracle_set_threads(int(n))
 
 
 def _p(a: Optional[np.ndarray]):

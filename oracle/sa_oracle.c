@@ -29,6 +29,11 @@
  *  [RK] also: the probe signal (keys sampled evenly inside a block, the
  *           largest dot product with the query as the block's score).
  *
+ * Threads: every function's outer loop runs over independent outputs (a page,
+ * a (b, kv-head) list or a query head), so it is an OpenMP parallel for; no
+ * value depends on the thread count.  oracle_set_threads() sets the count
+ * (the Python front end starts at 1).
+ *
  * Layouts (row-major):
  *   q        [B, Hq, d]              fp32 or bf16 bits
  *   K, V     [P, S, Hkv, d]          fp32, bf16 bits, or int8 codes
@@ -40,6 +45,9 @@
  * Query heads h*G .. h*G+G-1 share kv-head h (G = Hq / Hkv).
  */
 #include <math.h>
+#ifdef _OPENMP
+#include <omp.h>
+#endif
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -105,6 +113,27 @@ static size_t elem_size(int dtype) { return dtype == OR_F32 ? 4 : (dtype == OR_B
 
 static int ceil_div(int a, int b) { return (a + b - 1) / b; }
 
+/* Nonzero if a page-table entry of a referenced page (b, p < n_b) is out of range. */
+static int check_pages(const int32_t *page_table, const int32_t *seq_lens, int B, int max_pages,
+                       int S, int num_pages) {
+  for (int b = 0; b < B; ++b) {
+    int n = ceil_div(seq_lens[b], S);
+    for (int p = 0; p < n && p < max_pages; ++p) {
+      int pp = page_table[(size_t)b * max_pages + p];
+      if (pp < 0 || pp >= num_pages) return 1;
+    }
+  }
+  return 0;
+}
+
+void oracle_set_threads(int n) {
+#ifdef _OPENMP
+  omp_set_num_threads(n < 1 ? 1 : n);
+#else
+  (void)n;
+#endif
+}
+
 /* -------------------------------------------------- page metadata (min/max) */
 /*
  * [Quest] incremental update: inserting key k into a page sets
@@ -117,13 +146,14 @@ int oracle_quest_meta(const void *k, int dtype, int num_pages, int S, int hkv, i
                       const int32_t *page_table, const int32_t *seq_lens, int B, int max_pages,
                       void *meta) {
   if (dtype == OR_I8) return -1;
+  if (check_pages(page_table, seq_lens, B, max_pages, S, num_pages)) return -2;
   size_t es = elem_size(dtype);
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
   for (int b = 0; b < B; ++b) {
-    int L = seq_lens[b];
-    int n = ceil_div(L, S);
-    for (int p = 0; p < n && p < max_pages; ++p) {
+    for (int p = 0; p < max_pages; ++p) {
+      int L = seq_lens[b];
+      if (p >= ceil_div(L, S)) continue;
       int pp = page_table[(size_t)b * max_pages + p];
-      if (pp < 0 || pp >= num_pages) return -2;
       int valid = L - p * S < S ? L - p * S : S;
       for (int h = 0; h < hkv; ++h) {
         for (int i = 0; i < d; ++i) {
@@ -164,9 +194,10 @@ void oracle_quest_scores(const void *q, int q_dtype, int hq, const void *meta, i
                          const int32_t *seq_lens, int B, int max_pages, double *scores,
                          double *abs_scale) {
   int G = hq / hkv;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int b = 0; b < B; ++b) {
-    int n = ceil_div(seq_lens[b], S);
     for (int h = 0; h < hkv; ++h) {
+      int n = ceil_div(seq_lens[b], S);
       for (int p = 0; p < max_pages; ++p) {
         size_t o = ((size_t)b * hkv + h) * max_pages + p;
         if (p >= n) {
@@ -213,14 +244,15 @@ int oracle_sals_index(const void *k, int dtype, const uint16_t *k_scale, int num
                       int max_pages, const float *proj, int rank, uint8_t *codes,
                       uint16_t *scales) {
   if (rank % 2 != 0 || rank > 64 || d > 1024) return -1;
-  float khat[1024], kp[64];
+  if (check_pages(page_table, seq_lens, B, max_pages, S, num_pages)) return -2;
   int nb = rank / 2;
+#pragma omp parallel for collapse(2) schedule(dynamic, 16)
   for (int b = 0; b < B; ++b) {
-    int L = seq_lens[b];
-    int n = ceil_div(L, S);
-    for (int p = 0; p < n && p < max_pages; ++p) {
+    for (int p = 0; p < max_pages; ++p) {
+      float khat[1024], kp[64];
+      int L = seq_lens[b];
+      if (p >= ceil_div(L, S)) continue;
       int pp = page_table[(size_t)b * max_pages + p];
-      if (pp < 0 || pp >= num_pages) return -2;
       for (int s = 0; s < S; ++s) {
         for (int h = 0; h < hkv; ++h) {
           size_t row = ((size_t)pp * S + s) * hkv + h;
@@ -316,13 +348,14 @@ static void sals_scores_body(const void *q, int q_dtype, int hq, lowrank_key_fn 
                              double *abs_scale) {
   int G = hq / hkv;
   int max_units = ceil_div(max_pages * S, unit_tokens);
-  double *qbar = (double *)malloc(sizeof(double) * (size_t)d);
-  double *qt = (double *)malloc(sizeof(double) * (size_t)rank);
-  double *z = (double *)malloc(sizeof(double) * (size_t)unit_tokens);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int b = 0; b < B; ++b) {
-    int L = seq_lens[b];
-    int nu = ceil_div(L, unit_tokens);
     for (int h = 0; h < hkv; ++h) {
+      double *qbar = (double *)malloc(sizeof(double) * (size_t)d);
+      double *qt = (double *)malloc(sizeof(double) * (size_t)rank);
+      double *z = (double *)malloc(sizeof(double) * (size_t)unit_tokens);
+      int L = seq_lens[b];
+      int nu = ceil_div(L, unit_tokens);
       for (int i = 0; i < d; ++i) {
         double s = 0.0;
         for (int g = 0; g < G; ++g) s += q_value(q, q_dtype, ((size_t)b * hq + (size_t)h * G + g) * d + i);
@@ -357,11 +390,11 @@ static void sals_scores_body(const void *q, int q_dtype, int hq, lowrank_key_fn 
         scores[o] = log_sum_exp(z, t1 - t0);
         if (abs_scale) abs_scale[o] = amax + 1.0;
       }
+      free(qbar);
+      free(qt);
+      free(z);
     }
   }
-  free(qbar);
-  free(qt);
-  free(z);
 }
 
 /* SALS block scores from the int4 index key (codes + fp16 scales). */
@@ -409,14 +442,15 @@ int oracle_select(const double *scores, int B, int hkv, int max_units, const int
                   int S, int unit_tokens, int k, int n_head, int n_tail, int max_sel, int32_t *sel,
                   int32_t *num_sel) {
   int upu = unit_tokens / S;
-  struct unit_score *buf = (struct unit_score *)malloc(sizeof(struct unit_score) * (size_t)(max_units + 1));
-  unsigned char *keep = (unsigned char *)malloc((size_t)max_units + 1);
   int rc = 0;
+#pragma omp parallel for collapse(2) schedule(dynamic, 1) reduction(min : rc)
   for (int b = 0; b < B; ++b) {
-    int L = seq_lens[b];
-    int n = ceil_div(L, unit_tokens);
-    int np = ceil_div(L, S);
     for (int h = 0; h < hkv; ++h) {
+      struct unit_score *buf = (struct unit_score *)malloc(sizeof(struct unit_score) * (size_t)(max_units + 1));
+      unsigned char *keep = (unsigned char *)malloc((size_t)max_units + 1);
+      int L = seq_lens[b];
+      int n = ceil_div(L, unit_tokens);
+      int np = ceil_div(L, S);
       const double *sc = scores + ((size_t)b * hkv + h) * max_units;
       memset(keep, 0, (size_t)max_units + 1);
       if (n <= n_head + n_tail + k) {
@@ -444,10 +478,10 @@ int oracle_select(const double *scores, int B, int hkv, int max_units, const int
       }
       for (int r = cnt; r < max_sel; ++r) out[r] = -1;
       num_sel[(size_t)b * hkv + h] = cnt;
+      free(buf);
+      free(keep);
     }
   }
-  free(buf);
-  free(keep);
   return rc;
 }
 
@@ -471,10 +505,13 @@ void oracle_attention(const void *q, int q_dtype, int hq, const void *k, const v
   int G = hq / hkv;
   int total = rows ? nrows : B * hq;
   size_t cap = (size_t)max_pages * S;
+#pragma omp parallel
+  {
   double *z = (double *)malloc(sizeof(double) * (cap ? cap : 1));
   size_t *tok = (size_t *)malloc(sizeof(size_t) * (cap ? cap : 1));
   double *acc = (double *)malloc(sizeof(double) * (size_t)d);
   double *qrow = (double *)malloc(sizeof(double) * (size_t)d);
+#pragma omp for schedule(dynamic, 1)
   for (int r = 0; r < total; ++r) {
     int flat = rows ? rows[r] : r;
     int b = flat / hq, head = flat % hq, h = head / G;
@@ -518,6 +555,7 @@ void oracle_attention(const void *q, int q_dtype, int hq, const void *k, const v
   free(tok);
   free(acc);
   free(qrow);
+  }
 }
 
 /* ------------------------------------------------- probe-sampling scores
@@ -539,10 +577,11 @@ void oracle_probe_scores(const void *q, int q_dtype, int hq, const void *k, int 
                          double *scores, double *abs_scale) {
   int G = hq / hkv;
   int max_units = ceil_div(max_pages * S, unit_tokens);
+#pragma omp parallel for collapse(2) schedule(dynamic, 1)
   for (int b = 0; b < B; ++b) {
-    int L = seq_lens[b];
-    int nu = ceil_div(L, unit_tokens);
     for (int h = 0; h < hkv; ++h) {
+      int L = seq_lens[b];
+      int nu = ceil_div(L, unit_tokens);
       for (int u = 0; u < max_units; ++u) {
         size_t o = ((size_t)b * hkv + h) * max_units + u;
         if (u >= nu) {

@@ -60,7 +60,7 @@ EXPORTS = ["sa_version", "sa_status_string", "sa_meta_bytes", "sa_meta_scale_byt
            "sa_build_page_meta", "sa_append_kv", "sa_max_units", "sa_score_pages", "sa_max_selected",
            "sa_topk_pages", "sa_attn_workspace_size", "sa_sparse_decode_attn",
            "sa_attn_heads_workspace_size", "sa_sparse_decode_attn_heads",
-           "sa_decode_step_workspace_size", "sa_decode_step"]
+           "sa_decode_step_workspace_size", "sa_decode_step", "sa_stream_read"]
 
 
 def load(path: str = LIB_PATH):
@@ -90,6 +90,7 @@ def load(path: str = LIB_PATH):
         "sa_sparse_decode_attn_heads": (ctypes.c_int, [VP, I32, I32, KV, SQ, VP, VP, I32, F, VP, VP, SZ, VP]),
         "sa_decode_step_workspace_size": (SZ, [I32, KV, SQ, CF]),
         "sa_decode_step": (ctypes.c_int, [VP, I32, I32, KV, SQ, CF, VP, VP, F, VP, VP, VP, VP, SZ, VP]),
+        "sa_stream_read": (ctypes.c_int, [VP, SZ, VP, SZ, VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -221,13 +222,8 @@ def alloc_meta(kv: KVCache, cfg: SelectCfg):
 
 
 def alloc_workspace(nbytes: int, device) -> torch.Tensor:
-    """Zero-filled device workspace (sa_decode_step needs zeroed control words on first use)."""
+    """Zero-filled device workspace (sa_decode_step needs its hand-off words zero on first use)."""
     return torch.zeros(max(nbytes, 256), dtype=torch.uint8, device=device)
-
-
-def step_error_flag(workspace: torch.Tensor) -> int:
-    """The fused step's timeout flag (third 32-bit word of the workspace); 0 when healthy."""
-    return int(workspace[8:12].view(torch.int32).item())
 
 
 # ---------------------------------------------------------------- entry points
@@ -295,3 +291,9 @@ def sa_decode_step(q: torch.Tensor, kv: KVCache, seqs: Seqs, cfg: SelectCfg, met
                                  _ptr(meta), _ptr(meta_scale), softmax_scale, _ptr(out),
                                  _ptr(sel), _ptr(num_sel), _ptr(workspace), workspace.numel(),
                                  _stream(stream)), "sa_decode_step")
+
+
+def sa_stream_read(src: torch.Tensor, sink: torch.Tensor, stream=None) -> None:
+    """Measurement helper: one streaming read of every byte of src (see include/sa.h)."""
+    _check(load().sa_stream_read(_ptr(src), src.numel() * src.element_size(), _ptr(sink),
+                                 sink.numel(), _stream(stream)), "sa_stream_read")

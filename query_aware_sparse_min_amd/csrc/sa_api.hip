@@ -2,6 +2,7 @@
 // launch planning, then the kernels of sa_meta / sa_score / sa_topk / sa_attn.
 // Every check runs on the host before anything is enqueued, and no function
 // allocates, frees or synchronises.
+#include <stdlib.h>
 #include <string.h>
 
 #include <atomic>
@@ -115,21 +116,31 @@ int device_cus() {
   return n;
 }
 
-// Co-resident workgroups of the fused step kernel on the current device,
-// cached per (device, kv dtype, q dtype).
+// Co-resident workgroups of the fused step kernel on the current device
+// (0 when the kernel's build cannot show its residency: the separate kernels
+// run instead), cached per (device, kv dtype, q dtype, keys per thread).
 int resident_step_wgs(int kv_dtype, int q_dtype, int max_pages) {
-  static std::atomic<int> cache[64][8];
+  static std::atomic<int> cache[64][8];  // value + 1; 0 = not yet queried
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess || dev < 0) dev = 0;
   const int kpt = step_kpt(max_pages);
   const int slot = (kv_dtype == SA_F32 ? 0 : 2) + (q_dtype == SA_F32 ? 0 : 1) + (kpt > step_kpt(1) ? 4 : 0);
   if (dev < 64) {
     const int c = cache[dev][slot].load(std::memory_order_relaxed);
-    if (c > 0) return c;
+    if (c > 0) return c - 1;
   }
   const int n = step_resident_wgs(kv_dtype, q_dtype, kpt, device_cus());
-  if (dev < 64 && n > 0) cache[dev][slot].store(n, std::memory_order_relaxed);
+  if (dev < 64) cache[dev][slot].store(n + 1, std::memory_order_relaxed);
   return n;
+}
+
+// Optional cap on the fused step kernel's workgroups: the environment variable
+// SA_STEP_MAX_WORKGROUPS (a positive integer), read at every call; 0 = no cap.
+int step_wg_cap() {
+  const char* e = getenv("SA_STEP_MAX_WORKGROUPS");
+  if (!e || !*e) return 0;
+  const long v = strtol(e, nullptr, 10);
+  return v > 0 && v < (1L << 20) ? (int)v : 0;
 }
 
 constexpr int kPlanCUs = 256;  // task decomposition is planned for a 256-CU MI355X
@@ -161,7 +172,7 @@ HeadsLayout heads_layout(int B, int hq, int hkv, int max_pages, int max_sel) {
 }
 
 struct StepLayout {
-  size_t ctl, scores, sel, num_sel, partials, heads, total;
+  size_t arrive, scores, sel, num_sel, partials, heads, total;
   int max_units, max_sel;
   bool dense;  // every list keeps all of its units: no scoring needed
   bool fused;  // Quest: one persistent kernel for the whole step
@@ -187,8 +198,8 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
   const size_t fused_part = (size_t)L.splan.lists * L.splan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2);
   size_t off = 0;
-  L.ctl = off;
-  off = align_up(off + step_ctl_bytes());
+  L.arrive = off;  // the fused kernel's per-list arrival counters
+  off = align_up(off + (size_t)L.splan.lists * sizeof(uint32_t));
   L.scores = off;
   off = align_up(off + (L.dense ? 0 : lists * L.max_units * sizeof(float)));
   L.sel = off;
@@ -436,12 +447,10 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
                                        nullptr, 0, lay.plan, softmax_scale, partials, out, st));
   }
   float* scores = reinterpret_cast<float*>(ws + lay.scores);
-  int wgs = 0;
-  if (lay.fused) {
-    wgs = resident_step_wgs(kv->dtype, q_dtype, seqs->max_pages);
-    if (wgs < 1) wgs = device_cus();  // one workgroup per CU always fits
-  }
-  if (lay.fused && lay.splan.nc <= wgs) {
+  // the fused kernel's grid is the number of its workgroups the device holds at
+  // once (one per CU); a build that uses scratch memory runs the separate kernels
+  const int wgs = lay.fused ? resident_step_wgs(kv->dtype, q_dtype, seqs->max_pages) : 0;
+  if (lay.fused && wgs >= 1) {
     StepArgs A{};
     A.q = q;
     A.k = kv->k;
@@ -464,9 +473,11 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
     A.max_sel = lay.max_sel;
     A.partials = partials;
     A.out = out;
-    A.ctl = reinterpret_cast<StepCtl*>(ws + lay.ctl);
+    A.arrive = reinterpret_cast<uint32_t*>(ws + lay.arrive);
     StepPlan P = lay.splan;
+    const int cap = step_wg_cap();
     P.grid = P.n_tasks < wgs ? P.n_tasks : wgs;
+    if (cap > 0 && cap < P.grid) P.grid = cap;
     return hip_status(launch_quest_step(kv->dtype, q_dtype, A, P, st));
   }
   if (lay.per_head) {
@@ -509,6 +520,15 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale, kv->v_scale,
                                      s, seqs->page_table, seqs->seq_lens, sel_buf, num_buf,
                                      lay.max_sel, lay.plan, softmax_scale, partials, out, st));
+}
+
+int sa_stream_read(const void* src, size_t bytes, uint32_t* sink, size_t sink_words, void* stream) {
+  if (!src || !aligned16(src) || bytes == 0 || bytes % 16 != 0 || !sink || sink_words < 1)
+    return SA_ERR_INVALID_ARG;
+  // about eight workgroups per compute unit keep enough loads in flight
+  const size_t want = (size_t)device_cus() * 8;
+  const int grid = (int)(sink_words < want ? sink_words : want);
+  return hip_status(launch_stream_read(src, bytes, sink, grid, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

@@ -231,7 +231,7 @@ __global__ __launch_bounds__(kAttnThreads) void merge_kernel(const float* __rest
     first = (size_t)pre[b] + (size_t)h * ns;
   }
   merge_list(partials + first * G * kPartStride, ns, G,
-             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, lds, nullptr, g, 1);
+             out + ((size_t)b * hkv * G + (size_t)h * G) * kHeadDim, lds, g, 1);
 }
 
 template <int KT, int QT, bool PLAN>

@@ -162,9 +162,8 @@ struct WavePages {
 
 // Folds the NW waves' (max, sum, acc) of every query head, which every wave
 // has stored to sm.m / sm.l / sm.acc, into the workgroup's partial records
-// part[G][kPartStride].  COH: stored device-coherently; ENC: as (bits ^
-// kPartSentinel).  All threads call.
-template <int G, int NW, bool COH, bool ENC>
+// part[G][kPartStride].  COH: stored device-coherently.  All threads call.
+template <int G, int NW, bool COH>
 __device__ __forceinline__ void put_partials(AttnSmem<G, NW>& sm, float* __restrict__ part) {
   __syncthreads();
   for (int idx = threadIdx.x; idx < G * kHeadDim; idx += blockDim.x) {
@@ -181,10 +180,7 @@ __device__ __forceinline__ void put_partials(AttnSmem<G, NW>& sm, float* __restr
         ls = fmaf(sm.l[w][g], f, ls);
       }
     }
-    auto put = [&](int i, float x) {
-      if constexpr (ENC) st_x<COH>(reinterpret_cast<uint32_t*>(part) + i, __float_as_uint(x) ^ kPartSentinel);
-      else st_x<COH>(part + i, x);
-    };
+    auto put = [&](int i, float x) { st_x<COH>(part + i, x); };
     put(g * kPartStride + dim, a);
     if (dim == 0) {
       put(g * kPartStride + kHeadDim, M);
@@ -199,9 +195,8 @@ __device__ __forceinline__ void put_partials(AttnSmem<G, NW>& sm, float* __restr
 // already resolved to (physical page << 4) | (valid tokens - 1), read with
 // plain loads; the page table is then not read.
 // PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
-// COH: lst is read and the partials are written device-coherently; ENC: the
-// partial words are stored as (bits ^ kPartSentinel).
-template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4, bool ENC = false>
+// COH: lst is read and the partials are written device-coherently.
+template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4>
 __device__ __forceinline__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
                              const void* __restrict__ v, const uint16_t* __restrict__ ks,
                              const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
@@ -314,7 +309,7 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
       }
     }
   }
-  put_partials<G, NW, COH, ENC>(sm, part);
+  put_partials<G, NW, COH>(sm, part);
 }
 
 // ---------------------------------------------------------------- MFMA variant
@@ -500,7 +495,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 #pragma unroll
       for (int e = 0; e < 8; ++e) sm.acc[wave][g][8 * c + e] = acc[g][e];
   }
-  put_partials<G, NW, false, false>(sm, part);
+  put_partials<G, NW, false>(sm, part);
 }
 
 // Merge ns partial records part[ns][G][kPartStride] of one list into
@@ -510,14 +505,12 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 // group p folds splits p, p + P, p + 2P, ... into a running (M, acc, sum),
 // fetching C splits per memory round trip, and the groups are combined
 // through lds (3 * blockDim floats).  The order is fixed, so the result is
-// deterministic.  COH: partials are read device-coherently.  ENC: partials are
-// stored as (bits ^ kPartSentinel) by other workgroups, 0 while not yet
-// written; such words are re-read until they arrive (bounded; on timeout
-// *err |= 4).  All threads call.
-template <bool COH = false, bool ENC = false, int C = 16>
+// deterministic.  COH: partials are read device-coherently (written by other
+// workgroups of the same launch).  All threads call.
+template <bool COH = false, int C = 16>
 __device__ __forceinline__ void merge_list(const float* __restrict__ part, int ns, int G,
                                            float* __restrict__ out, float* __restrict__ lds,
-                                           uint32_t* err = nullptr, int g0 = 0, int gn = -1) {
+                                           int g0 = 0, int gn = -1) {
   if (gn < 0) gn = G;
   out += (size_t)g0 * kHeadDim;
   const int no = gn * kHeadDim;
@@ -528,48 +521,12 @@ __device__ __forceinline__ void merge_list(const float* __restrict__ part, int n
     const int g = g0 + o / kHeadDim, dim = o % kHeadDim;
     for (int s0 = first; s0 < ns; s0 += C * step) {
       float av[C], mv[C], lv[C];
-      if constexpr (ENC) {
-        const uint32_t* pw = reinterpret_cast<const uint32_t*>(part);
-        uint32_t aw[C], mw[C], lw[C];
-        auto rec = [&](int j) { return ((size_t)min(s0 + j * step, ns - 1) * G + g) * kPartStride; };
 #pragma unroll
-        for (int j = 0; j < C; ++j) {  // unconditional loads (clamped split) stay in flight together
-          aw[j] = ld_x<true>(pw + rec(j) + dim);
-          mw[j] = ld_x<true>(pw + rec(j) + kHeadDim);
-          lw[j] = ld_x<true>(pw + rec(j) + kHeadDim + 1);
-        }
-        bool missing = false;
-#pragma unroll
-        for (int j = 0; j < C; ++j) missing |= (aw[j] == 0u) | (mw[j] == 0u) | (lw[j] == 0u);
-        for (uint32_t spins = 0; missing; ++spins) {  // records not yet landed: re-read those words
-          if (spins > kPollLimit) {
-            if (err) __hip_atomic_fetch_or(err, 4u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-          __builtin_amdgcn_s_sleep(1);
-          missing = false;
-#pragma unroll
-          for (int j = 0; j < C; ++j) {
-            if (aw[j] == 0u) aw[j] = ld_x<true>(pw + rec(j) + dim);
-            if (mw[j] == 0u) mw[j] = ld_x<true>(pw + rec(j) + kHeadDim);
-            if (lw[j] == 0u) lw[j] = ld_x<true>(pw + rec(j) + kHeadDim + 1);
-            missing |= (aw[j] == 0u) | (mw[j] == 0u) | (lw[j] == 0u);
-          }
-        }
-#pragma unroll
-        for (int j = 0; j < C; ++j) {
-          av[j] = __uint_as_float(aw[j] ^ kPartSentinel);
-          mv[j] = __uint_as_float(mw[j] ^ kPartSentinel);
-          lv[j] = __uint_as_float(lw[j] ^ kPartSentinel);
-        }
-      } else {
-#pragma unroll
-        for (int j = 0; j < C; ++j) {  // unconditional loads (clamped split) stay in flight together
-          const float* rec = part + ((size_t)min(s0 + j * step, ns - 1) * G + g) * kPartStride;
-          av[j] = ld_x<COH>(rec + dim);
-          mv[j] = ld_x<COH>(rec + kHeadDim);
-          lv[j] = ld_x<COH>(rec + kHeadDim + 1);
-        }
+      for (int j = 0; j < C; ++j) {  // unconditional loads (clamped split) stay in flight together
+        const float* rec = part + ((size_t)min(s0 + j * step, ns - 1) * G + g) * kPartStride;
+        av[j] = ld_x<COH>(rec + dim);
+        mv[j] = ld_x<COH>(rec + kHeadDim);
+        lv[j] = ld_x<COH>(rec + kHeadDim + 1);
       }
 #pragma unroll
       for (int j = 0; j < C; ++j)

@@ -37,6 +37,21 @@ namespace sa {
 constexpr int kTopkDigit = 8;
 constexpr int kTopkBins = 1 << kTopkDigit;
 
+// The KEYS hand-off's fallback when a key has not arrived in time: the
+// caller's help object produces the missing keys itself.  mark(u) is called by
+// every thread for each of its units still missing (u in [n_head, n - n_tail)),
+// then, after a barrier, run() by all NT threads; run() must have stored every
+// marked unit's key, device-coherently and completed, before it returns.
+struct NoHelp {
+  __device__ __forceinline__ void mark(int) const {}
+  __device__ __forceinline__ void run() const {}
+};
+
+// How long a KEYS reader polls for keys still at 0 before it asks for help:
+// s_memrealtime ticks (100 MHz), about 20 us, far above the usual spread of
+// a few microseconds between the first and the last chunk of a list.
+constexpr uint64_t kKeyWaitTicks = 2000;
+
 template <int NT>
 struct TopkSmem {
   alignas(16) uint32_t hist[3][kTopkBins];
@@ -52,12 +67,14 @@ struct TopkSmem {
 // unless exact ties need it.  KPT > 0 requires n - n_head - n_tail <= NT * KPT.
 // COH: the scores are read device-coherently.  KEYS (KPT > 0 only): sc holds
 // order_key() words written by other workgroups, 0 while not yet written; such
-// words are re-read until they arrive (bounded; on timeout *err |= 2).  All NT
-// threads call; sm is free again on return once the caller has synchronised.
-template <int NT, int KPT, bool COH, bool KEYS = false, typename Keep>
+// words are re-read for up to kKeyWaitTicks, and any still missing then are
+// produced through help (so the call never depends on another workgroup
+// being resident).  All NT threads call; sm is free again on return once the
+// caller has synchronised.
+template <int NT, int KPT, bool COH, bool KEYS = false, typename Keep, typename Help = NoHelp>
 __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, int k, int n_head,
                                           int n_tail, TopkSmem<NT>& sm, Keep&& keep,
-                                          bool want_rank = true, uint32_t* err = nullptr) {
+                                          bool want_rank = true, const Help& help = Help{}) {
   static_assert(!KEYS || KPT > 0, "key hand-off needs register-resident keys");
   constexpr int NW = NT / 64;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -83,20 +100,30 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
     bool missing = false;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) missing |= j < cnt_t && key[j] == 0u;
-    for (uint32_t spins = 0; missing; ++spins) {  // stores not yet landed: re-read those words
-      if (spins > kPollLimit) {
-        if (err) __hip_atomic_fetch_or(err, 2u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        break;
-      }
-      __builtin_amdgcn_s_sleep(1);
-      missing = false;
+    if (missing) {  // stores not yet landed: re-read those words, for a bounded time
+      const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kKeyWaitTicks;
+      while (missing && __builtin_amdgcn_s_memrealtime() < t_end) {
+        __builtin_amdgcn_s_sleep(1);
+        missing = false;
 #pragma unroll
-      for (int j = 0; j < KPT; ++j) {
-        if (j < cnt_t && key[j] == 0u) {
-          key[j] = ld_x<true>(mk + r0 + j);
-          missing |= key[j] == 0u;
+        for (int j = 0; j < KPT; ++j) {
+          if (j < cnt_t && key[j] == 0u) {
+            key[j] = ld_x<true>(mk + r0 + j);
+            missing |= key[j] == 0u;
+          }
         }
       }
+    }
+    if (__syncthreads_or(missing ? 1 : 0)) {  // still missing: their units are produced here
+#pragma unroll
+      for (int j = 0; j < KPT; ++j)
+        if (j < cnt_t && key[j] == 0u) help.mark(n_head + r0 + j);
+      __syncthreads();
+      help.run();
+      __syncthreads();
+      // every key is read again, so that none is held in registers while help runs
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) key[j] = ld_x<true>(mk + min(r0 + j, m - 1));
     }
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? key[j] : 0u;

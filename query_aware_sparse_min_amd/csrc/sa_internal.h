@@ -160,12 +160,6 @@ __device__ __forceinline__ uint32_t order_key(float f) {
   return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
-// Partial records handed between workgroups are stored as (bits ^ kPartSentinel):
-// the sentinel is a NaN payload no partial value takes, so a zero word is one
-// that has not been written yet, and zero-filled memory reads as "absent".
-constexpr uint32_t kPartSentinel = 0x7FC0DEADu;
-constexpr uint32_t kPollLimit = 1u << 18;  // bounded re-polls of a not-yet-written word
-
 // Wait until this thread's stores have completed (s_waitcnt vmcnt(0)); the
 // signal fences keep the compiler from moving memory accesses across it.
 __device__ __forceinline__ void stores_done() {
@@ -223,6 +217,10 @@ constexpr int kUnionPages = 16384;  // largest max_pages the union supports
 hipError_t launch_union(const int32_t* sel, const int32_t* num_sel, int max_sel, const Shapes& s,
                         const int32_t* lens, int32_t* ulist, int32_t* ucount, int umax,
                         hipStream_t st);
+
+// Streaming read of bytes (a multiple of 16) at src by grid workgroups; sink
+// holds grid words (written only in a case no realistic input reaches).
+hipError_t launch_stream_read(const void* src, size_t bytes, uint32_t* sink, int grid, hipStream_t st);
 
 hipError_t launch_attention(int kv_dtype, int q_dtype, const void* q, const void* k,
                             const void* v, const uint16_t* k_scale, const uint16_t* v_scale,

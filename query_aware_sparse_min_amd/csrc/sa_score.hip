@@ -130,8 +130,9 @@ __global__ __launch_bounds__(256) void quest_score_mfma_kernel(
 
 constexpr int kSalsUnitsPerWG = 8;  // blocks scored per workgroup, two per wave
 constexpr int kQbarStride = kHeadDim + 4;  // padded rows: the MFMA reads 16 rows at one column
-constexpr int kQDigits = 6;         // balanced base-16 digits of the fixed-point index query
-constexpr int kQFracBits = 22;      // |Q| < 2^22 (six balanced digits reach 7.8e6)
+constexpr int kQDigits = 7;         // balanced base-16 digits of the fixed-point index query
+constexpr int kQLoDigits = 4;       // digits summed into the low int32 partial
+constexpr int kQFracBits = 26;      // |Q| <= 2^26 (seven balanced digits reach 1.25e8)
 __host__ __device__ constexpr size_t sals_smem_bytes(int hkv) {
   return sizeof(float) * ((size_t)kHeadDim * kRank + (size_t)hkv * kQbarStride) +
          sizeof(uint32_t) * (size_t)hkv * (2 * kQDigits + 1);
@@ -152,11 +153,15 @@ __device__ __forceinline__ void lse_merge(float& m, float& s, float m2, float s2
 // stages the batch row of q and the projection P in LDS (vector loads, one
 // memory round trip), forms every kv-head's group-mean query and projects it,
 // qt = qbar P, on the matrix cores (fp32 v_mfma_f32_16x16x4f32, 16 kv-heads
-// per tile).  Each kv-head's qt becomes integers Q_j = rint(qt_j 2^(22-e)),
-// 2^(e-1) <= max |qt_j| < 2^e, written as six balanced base-16 digits packed
+// per tile).  Each kv-head's qt becomes integers Q_j = rint(qt_j 2^(26-e)),
+// 2^(e-1) <= max |qt_j| < 2^e, written as seven balanced base-16 digits packed
 // as signed nibbles; a token's dot product with its sixteen int4 codes is then
-// exact integer work (twelve v_dot8_i32_i4, Horner over the digits), scaled by
-// 2^(e-22).  Lane l then takes kv-head l % 8 of a group of kSalsHeads and
+// exact integer work (fourteen v_dot8_i32_i4, Horner over the high three and
+// the low four digits into two int32 sums, so neither can overflow), joined
+// by one fp32 fma (the only rounding) and scaled by 2^(e-26).  The rounding of
+// Q moves a token's score by at most sum_j |c_j| 2^(e-27) scale, i.e. by at
+// most 2^-22 of the token's own magnitude sum_j |qt_j c_j| scale when the
+// codes are saturated at +-7.  Lane l then takes kv-head l % 8 of a group of kSalsHeads and
 // token slot l / 8; a wave scores its two blocks together: per 64-token pass it
 // reads the page-table entries of its 16 tokens, then their code words and
 // scales (the 8 lanes of a slot read one token's 64 contiguous bytes), and
@@ -174,7 +179,7 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
   float* proj_s = sals_smem;                      // [d][rank]
   float* qbar = proj_s + kHeadDim * kRank;        // [hkv][kQbarStride] group-mean query
   // [hkv][kQDigits][2] digit words of the projected index query (columns 0-7,
-  // 8-15), then [hkv] scales 2^(e-22)
+  // 8-15), then [hkv] scales 2^(e-26)
   uint32_t* qd_s = reinterpret_cast<uint32_t*>(qbar + hkv * kQbarStride);
   float* qf_s = reinterpret_cast<float*>(qd_s + hkv * 2 * kQDigits);
   const int b = blockIdx.y;
@@ -292,7 +297,7 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       (void)frexpf(max16(fabsf(c[i])), &ex[i]);
-      const uint32_t u = (uint32_t)((int)rintf(ldexpf(c[i], kQFracBits - ex[i])) + 0x888888);
+      const uint32_t u = (uint32_t)((int)rintf(ldexpf(c[i], kQFracBits - ex[i])) + 0x8888888);
 #pragma unroll
       for (int k = 0; k < kQDigits; ++k) w[i][k] = (((u >> (4 * k)) & 15u) ^ 8u) << (4 * (j & 7));
     }
@@ -333,13 +338,30 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
         issue_pt(t0);
         issue_codes(hh);
       }
-      // sum_j c_j Q_j per token, exact (|.| < 7 * 16 * 2^22): Horner over the
-      // digits, the 16 tokens interleaved
+      // sum_j c_j Q_j per token: Horner over the high digits (|.| < 7 * 16 *
+      // 0x888) and over the low digits (|.| < 7 * 16 * 0x8888), each exact in
+      // int32 and in fp32, then hi * 16^4 + lo with one rounding; the 16
+      // tokens interleaved
       int dot[16];
+      float dotf[16];
 #pragma unroll
       for (int ii = 0; ii < 16; ++ii) dot[ii] = 0;
 #pragma unroll
-      for (int k = kQDigits - 1; k >= 0; --k) {
+      for (int k = kQDigits - 1; k >= kQLoDigits; --k) {
+#pragma unroll
+        for (int ii = 0; ii < 16; ++ii) {
+          dot[ii] = __builtin_amdgcn_sdot8((int)cw[ii].x, (int)qd[k].x, dot[ii], false);
+          dot[ii] = __builtin_amdgcn_sdot8((int)cw[ii].y, (int)qd[k].y, dot[ii], false);
+          if (k > kQLoDigits) dot[ii] = (int)((uint32_t)dot[ii] << 4);
+        }
+      }
+#pragma unroll
+      for (int ii = 0; ii < 16; ++ii) {
+        dotf[ii] = (float)dot[ii];
+        dot[ii] = 0;
+      }
+#pragma unroll
+      for (int k = kQLoDigits - 1; k >= 0; --k) {
 #pragma unroll
         for (int ii = 0; ii < 16; ++ii) {
           dot[ii] = __builtin_amdgcn_sdot8((int)cw[ii].x, (int)qd[k].x, dot[ii], false);
@@ -348,12 +370,14 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
         }
       }
 #pragma unroll
+      for (int ii = 0; ii < 16; ++ii) dotf[ii] = fmaf(dotf[ii], 65536.0f, (float)dot[ii]);
+#pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         float z[8], zmax = -INFINITY;
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
           const int ii = 8 * blk + i;
-          const float zv = fz * (f16_to_f32(sw[ii]) * (float)dot[ii]);
+          const float zv = fz * (f16_to_f32(sw[ii]) * dotf[ii]);
           z[i] = (ok[ii] && hv) ? zv : -INFINITY;
           zmax = fmaxf(zmax, z[i]);
         }

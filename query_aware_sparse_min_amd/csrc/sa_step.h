@@ -12,18 +12,12 @@ constexpr int kStepMaxPages = 4096;          // top-K keys of a list stay in reg
 constexpr int kStepMaxPhysPages = 1 << 27;   // resolved pages pack the page id in 27 bits
 constexpr int kStepMaxChunk = 1024;          // pages per chunk task (kept in LDS)
 
-// Control word record at the head of the step workspace.
-struct StepCtl {
-  uint32_t reserved[2];
-  uint32_t error;  // nonzero after a bounded wait timed out
-  uint32_t pad[13];
-};
 struct StepPlan {
   int lists;        // B * Hkv
-  int chunk_pages;  // pages per chunk task (multiple of 64, <= kStepMaxChunk)
+  int chunk_pages;  // pages per chunk task (multiple of 16, <= kStepMaxChunk)
   int nc;           // chunk tasks per list
   int n_tasks;      // lists * nc
-  int grid;         // workgroups launched: all co-resident, and >= nc
+  int grid;         // workgroups launched (about the resident count; any value >= 1 is correct)
 };
 
 struct StepArgs {
@@ -42,15 +36,15 @@ struct StepArgs {
   int max_sel;
   float* partials;  // [lists][nc][G][kHeadDim + 2]
   float* out;       // [B][hq][kHeadDim]
-  StepCtl* ctl;
+  uint32_t* arrive; // [lists] chunks of the list done so far (0 between calls)
 };
 
 StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_cus);
-// Workgroups of the fused kernel that fit on the device at once (0 on error).
+// Workgroups of the fused kernel that fit on the device at once (0 on error,
+// or when the build uses scratch memory: the separate kernels run instead).
 int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus);
 // Top-K keys per thread of the fused kernel for lists of up to max_pages pages.
 int step_kpt(int max_pages);
-size_t step_ctl_bytes();
 hipError_t launch_quest_step(int kv_dtype, int q_dtype, const StepArgs& A, const StepPlan& P,
                              hipStream_t st);
 

@@ -13,26 +13,28 @@
 //      selected pages of its own chunk (writing their entries of the optional
 //      page list at their global ranks);
 //   3. attend to those pages (online softmax) and store one partial record;
-//   4. chunk 0 merges the list's nc partial records into out and clears the
-//      list's keys and partials.
+//   4. count itself done on the list's arrival counter; the chunk that
+//      arrives last merges the list's nc partial records into out and returns
+//      the list's keys and counter to 0.
 // So only the scores cross between workgroups before the attention, and the
 // page table is read once per page.
 //
-// Hand-offs need no counters: every handed-off word is nonzero once written
-// (order keys; partial words XOR a constant that no fp32 result takes), the
-// workspace holds zeros before the call, and a reader re-reads, device-
-// coherently, every word still 0 until all have arrived.  Stores are relaxed
-// and device-coherent (sc1) and nobody waits for them to land.  Every re-read
-// loop is bounded: on timeout ctl.error is set and the kernel still finishes.
-// The keys and partials of a list are returned to 0 by its merger, which runs
-// only after every chunk of the list has stored its partial record and so has
-// finished reading keys.
-//
-// Scheduling: task t runs on workgroup t mod grid, in order; every workgroup
-// is co-resident and grid >= nc.  A task waits only for the other chunks of
-// its own list, which sit on other workgroups (nc <= grid) behind tasks of
-// earlier lists only; the earliest unfinished list therefore always makes
-// progress, and the schedule cannot deadlock.
+// No workgroup ever waits for another one, so the kernel is correct whatever
+// subset of its grid is resident at a time:
+//  - keys: every key word is nonzero once written (order keys), the workspace
+//    holds zeros before the call, and a reader re-reads, device-coherently,
+//    every word still 0 -- for a bounded time.  Keys still missing then are
+//    computed by the reader itself: it scores the missing chunks with the same
+//    device code, so the words it stores are bit-identical to the owner's, and
+//    every chunk of the list sees the same keys whichever workgroup wrote them.
+//  - partial records: each chunk stores its record device-coherently, waits
+//    until the stores have completed, and only then increments the counter, so
+//    the chunk that sees nc - 1 reads every record complete.  Its own key
+//    stores have completed by then as well, so once the last chunk clears the
+//    keys no late key store of this call can follow.
+// Task t runs on workgroup t mod grid; the grid is about the number of
+// workgroups the device holds at once (one per CU), so normally every chunk of
+// a list is resident together and nobody computes another chunk's scores.
 #include "sa_dev_score.h"
 #include "sa_dev_topk.h"
 #include "sa_step.h"
@@ -53,7 +55,27 @@ union StepSmem {
   float merge[3 * kStepThreads];
 };
 
-// KPT: top-K keys per thread in registers (lists of up to 256 * KPT pages).
+// Keys of a list that have not arrived in time: the chunks that hold them are
+// scored again here (topk_core's help protocol).  mark() records the chunk of
+// a missing unit in an LDS bit mask; run() scores every marked chunk with the
+// same code the chunk's own task runs, stores the keys and waits for them.
+template <typename ScoreChunk>
+struct StepHelp {
+  uint32_t* mask;  // LDS, one bit per chunk of the list
+  int chunk_pages, nc;
+  ScoreChunk score_chunk;
+  __device__ __forceinline__ void mark(int u) const {
+    const int c = u / chunk_pages;
+    atomicOr(&mask[c >> 5], 1u << (c & 31));
+  }
+  __device__ __forceinline__ void run() const {
+    for (int c = 0; c < nc; ++c)
+      if ((mask[c >> 5] >> (c & 31)) & 1u) score_chunk(c);
+    stores_done();
+  }
+};
+
+// KPT: top-K keys per thread in registers (lists of up to 768 * KPT pages).
 template <int KT, int QT, int G, int KPT>
 __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A, StepPlan P) {
   __shared__ StepSmem<G> sm;
@@ -61,7 +83,8 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
   // chunk page kept by the selection: (physical << 4) | (valid - 1), else -1
   __shared__ int32_t s_kept[kStepMaxChunk];
   __shared__ int32_t s_list[kStepMaxChunk];  // kept pages: (physical << 4) | (valid - 1)
-  __shared__ int s_cnt;
+  __shared__ uint32_t s_help[kStepMaxPages / kChunkGrain / 32];  // chunks whose keys are missing
+  __shared__ int s_cnt, s_last;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int hq = A.hkv * G;
 
@@ -72,30 +95,46 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     const int c0 = c * P.chunk_pages;
     float* sc_row = A.scores + (size_t)i * A.max_pages;
 
-    // 1. scores of the chunk; the passes cover the chunk up to the page-table
-    // row length, so their loads need not wait for the sequence length
-    const int c_end = min(c0 + P.chunk_pages, A.max_pages);
-    int n = 0;
-    for (int p0 = c0; p0 < c_end; p0 += kScorePass)
-      n = quest_score_range<KT, QT, G, kScoreIT, true, kStepWaves, true>(A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row,
-                                                       p0, min(p0 + kScorePass, c_end), A.lens + b,
-                                                       A.max_pages, sc_row, s_pp + (p0 - c0));
+    // scores of chunk cc stored as order keys, IT page pairs per lane and pass;
+    // the passes cover the chunk up to the page-table row length, so their
+    // loads need not wait for the sequence length.  A page's key does not
+    // depend on IT (sixteen lanes of one row reduce it in a fixed order).
+    // Returns the list's page count.
+    auto score_chunk = [&](auto it_c, int cc, int32_t* pp_out) {
+      constexpr int IT = decltype(it_c)::value, kPass = 4 * kStepWaves * IT;
+      const int a0 = cc * P.chunk_pages, a1 = min(a0 + P.chunk_pages, A.max_pages);
+      int nv = 0;
+      for (int p0 = a0; p0 < a1; p0 += kPass)
+        nv = quest_score_range<KT, QT, G, IT, true, kStepWaves, true>(
+            A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row, p0, min(p0 + kPass, a1), A.lens + b,
+            A.max_pages, sc_row, pp_out ? pp_out + (p0 - a0) : nullptr);
+      return nv;
+    };
+    // the help path scores with one page pair per lane: fewer registers live
+    // beside the selection's
+    auto help_chunk = [&](int cc) { score_chunk(std::integral_constant<int, 1>{}, cc, nullptr); };
+
+    // 1. scores of the chunk
+    int n = score_chunk(std::integral_constant<int, kScoreIT>{}, c, s_pp);
     const int L = clamp_len(A.lens[b], A.max_pages);
-    if (c0 >= c_end) n = (L + kPage - 1) / kPage;
+    if (c0 >= A.max_pages) n = (L + kPage - 1) / kPage;
     const int c1 = min(c0 + P.chunk_pages, n);  // c1 <= c0: an empty chunk
     for (int j = tid; j < P.chunk_pages; j += kStepThreads) s_kept[j] = -1;
+    for (int j = tid; j < (int)(sizeof(s_help) / sizeof(s_help[0])); j += kStepThreads) s_help[j] = 0u;
     __syncthreads();  // the clears (and s_pp) before the selection marks kept pages
 
-    // 2. the list's selection (its keys re-read until all have arrived); keep this chunk's part
+    // 2. the list's selection (its keys re-read until all have arrived, or
+    // scored here); keep this chunk's part
     int32_t* sel_row = A.sel ? A.sel + (size_t)i * A.max_sel : nullptr;
+    const StepHelp<decltype(help_chunk)> help{s_help, P.chunk_pages, P.nc, help_chunk};
     topk_core<kStepThreads, KPT, true, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
-                                       [&](int rank, int u) {
-                                         if (u >= c0 && u < c1) {
-                                           const int pp = s_pp[u - c0];
-                                           if (pp >= 0) s_kept[u - c0] = (pp << 4) | (min(kPage, L - u * kPage) - 1);
-                                           if (sel_row && rank < A.max_sel) sel_row[rank] = u;
-                                         }
-                                       }, sel_row != nullptr, &A.ctl->error);
+                                             [&](int rank, int u) {
+                                               if (u >= c0 && u < c1) {
+                                                 const int pp = s_pp[u - c0];
+                                                 if (pp >= 0) s_kept[u - c0] = (pp << 4) | (min(kPage, L - u * kPage) - 1);
+                                                 if (sel_row && rank < A.max_sel) sel_row[rank] = u;
+                                               }
+                                             }, sel_row != nullptr, help);
     if (sel_row && c == 0) {  // count and padding of the optional page list
       const int cnt = min(min(n, A.n_head + A.k_compete + A.n_tail), A.max_sel);
       for (int j = cnt + tid; j < A.max_sel; j += kStepThreads) sel_row[j] = -1;
@@ -126,20 +165,21 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
 
     // 3. attention over the chunk's kept pages
     float* part_list = A.partials + (size_t)i * P.nc * G * kPartStride;
-    attend_range<KT, QT, G, 1, true, kStepWaves, true>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
-                                     pt_row, L, nullptr, 0, s_cnt, A.scale_log2,
-                                     part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
-    // 4. chunk 0 merges the list's partial records as they arrive
-    if (c == 0) {
-      __syncthreads();  // the attention's shared memory is free before the merge reuses it
-      merge_list<true, true, 4>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim,
-                             sm.merge, &A.ctl->error);
-      // every chunk of this list has read the list's keys (before storing its
-      // partial record): return keys and partials to the unwritten state (0)
+    attend_range<KT, QT, G, 1, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
+                                                 pt_row, L, nullptr, 0, s_cnt, A.scale_log2,
+                                                 part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
+    // 4. arrival: every store of this task has completed before the count
+    stores_done();
+    __syncthreads();
+    if (tid == 0)
+      s_last = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+               (uint32_t)(P.nc - 1);
+    __syncthreads();
+    if (s_last) {  // the list's last chunk: merge, then return keys and counter to 0
+      merge_list<true, 4>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim, sm.merge);
       uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
       for (int j = tid; j < A.max_pages; j += kStepThreads) st_x<true>(kw + j, 0u);
-      uint32_t* pw = reinterpret_cast<uint32_t*>(part_list);
-      for (int j = tid; j < P.nc * G * kPartStride; j += kStepThreads) st_x<true>(pw + j, 0u);
+      if (tid == 0) st_x<true>(A.arrive + i, 0u);
     }
     __syncthreads();  // shared memory is reused by the next task
   }
@@ -149,22 +189,17 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
 constexpr int kKptLo = (2048 + kStepThreads - 1) / kStepThreads;
 constexpr int kKptHi = (kStepMaxPages + kStepThreads - 1) / kStepThreads;
 
-template <int KT, int QT>
-hipError_t step_dispatch(int kpt, const StepArgs& A, const StepPlan& P, hipStream_t st) {
-  if (kpt <= kKptLo)
-    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, kKptLo>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
-  else
-    hipLaunchKernelGGL((quest_step_kernel<KT, QT, 1, kKptHi>), dim3(P.grid), dim3(kStepThreads), 0, st, A, P);
-  return hipGetLastError();
-}
+typedef void (*StepKernel)(StepArgs, StepPlan);
 
 template <int KT, int QT>
-int resident_of(int kpt) {
-  int per_cu = 0;
-  const hipError_t e = kpt <= kKptLo
-      ? hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, kKptLo>, kStepThreads, 0)
-      : hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, quest_step_kernel<KT, QT, 1, kKptHi>, kStepThreads, 0);
-  return e == hipSuccess ? per_cu : 0;
+StepKernel step_kernel_of(int kpt) {
+  return kpt <= kKptLo ? quest_step_kernel<KT, QT, 1, kKptLo> : quest_step_kernel<KT, QT, 1, kKptHi>;
+}
+
+StepKernel kernel_of(int kv_dtype, int q_dtype, int kpt) {
+  if (kv_dtype == SA_F32)
+    return q_dtype == SA_F32 ? step_kernel_of<SA_F32, SA_F32>(kpt) : step_kernel_of<SA_F32, SA_BF16>(kpt);
+  return q_dtype == SA_F32 ? step_kernel_of<SA_BF16, SA_F32>(kpt) : step_kernel_of<SA_BF16, SA_BF16>(kpt);
 }
 
 }  // namespace
@@ -188,27 +223,26 @@ StepPlan plan_step(int B, int Hq, int Hkv, int max_pages, int max_sel, int num_c
   return P;
 }
 
-size_t step_ctl_bytes() { return sizeof(StepCtl); }
-
 int step_kpt(int max_pages) { return max_pages <= kStepThreads * kKptLo ? kKptLo : kKptHi; }
 
 int step_resident_wgs(int kv_dtype, int q_dtype, int kpt, int num_cus) {
-  int per_cu;
-  if (kv_dtype == SA_F32)
-    per_cu = q_dtype == SA_F32 ? resident_of<SA_F32, SA_F32>(kpt) : resident_of<SA_F32, SA_BF16>(kpt);
-  else
-    per_cu = q_dtype == SA_F32 ? resident_of<SA_BF16, SA_F32>(kpt) : resident_of<SA_BF16, SA_BF16>(kpt);
+  const StepKernel f = kernel_of(kv_dtype, q_dtype, kpt);
+  // a build that spills keeps per-wave scratch, which the occupancy query does
+  // not count and which can hold back waves: 0 then sends the step to the
+  // separate kernels (the fused kernel would still be correct, but slow)
+  hipFuncAttributes fa{};
+  if (hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(f)) != hipSuccess || fa.localSizeBytes != 0)
+    return 0;
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, kStepThreads, 0) != hipSuccess) return 0;
   return per_cu < 1 ? 0 : per_cu * num_cus;
 }
 
 hipError_t launch_quest_step(int kv_dtype, int q_dtype, const StepArgs& A, const StepPlan& P,
                              hipStream_t st) {
-  const int kpt = step_kpt(A.max_pages);
-  if (kv_dtype == SA_F32)
-    return q_dtype == SA_F32 ? step_dispatch<SA_F32, SA_F32>(kpt, A, P, st)
-                             : step_dispatch<SA_F32, SA_BF16>(kpt, A, P, st);
-  return q_dtype == SA_F32 ? step_dispatch<SA_BF16, SA_F32>(kpt, A, P, st)
-                           : step_dispatch<SA_BF16, SA_BF16>(kpt, A, P, st);
+  hipLaunchKernelGGL(kernel_of(kv_dtype, q_dtype, step_kpt(A.max_pages)), dim3(P.grid), dim3(kStepThreads), 0,
+                     st, A, P);
+  return hipGetLastError();
 }
 
 }  // namespace sa

@@ -233,3 +233,14 @@ def test_per_head_checks():
     assert call(big) == sa.SA_ERR_UNSUPPORTED
     assert lib.sa_decode_step_workspace_size(32, ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(ph)) > \
         lib.sa_decode_step_workspace_size(32, ctypes.byref(kv), ctypes.byref(seqs), ctypes.byref(_cfg()))
+
+
+def test_stream_read_argument_checks():
+    lib = _lib()
+    assert lib.sa_stream_read(None, 1024, ctypes.c_void_p(FAKE), 8, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sa_stream_read(ctypes.c_void_p(FAKE + 4), 1024, ctypes.c_void_p(FAKE), 8, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sa_stream_read(ctypes.c_void_p(FAKE), 1000, ctypes.c_void_p(FAKE), 8, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sa_stream_read(ctypes.c_void_p(FAKE), 0, ctypes.c_void_p(FAKE), 8, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sa_stream_read(ctypes.c_void_p(FAKE), 1024, None, 8, None) == sa.SA_ERR_INVALID_ARG
+    assert lib.sa_stream_read(ctypes.c_void_p(FAKE), 1024, ctypes.c_void_p(FAKE), 0, None) == sa.SA_ERR_INVALID_ARG
+

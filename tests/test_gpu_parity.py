@@ -7,8 +7,8 @@ import torch
 import oracle
 import query_aware_sparse_min_amd as sa
 import synth
-from sa_testlib import (GpuCase, attn_tol, check_attention, check_scores, check_selection,
-                        meta_np, oracle_rows_for_lists)
+from sa_testlib import (GpuCase, assert_handoff_words_clear, attn_tol, check_attention,
+                        check_scores, check_selection, meta_np, oracle_rows_for_lists)
 
 pytestmark = pytest.mark.gpu
 
@@ -50,6 +50,12 @@ CASES = {
     # a list of 18750 pages: the top-K that re-reads its keys from the scores
     "gqa2_bf16_18k_pages": dict(B=1, Hq=2, Hkv=1, lens=(300000,), kv_dtype="bf16",
                                 q_dtype="bf16", budget_pages=64),
+    # the fused step with lists of 2305..4096 pages (six register keys per thread):
+    # one query head per kv-head, Quest, random page tables, bf16 and fp32
+    "mha_bf16_64k_kpt6": dict(B=2, Hq=2, Hkv=2, lens=(65536, 40000), kv_dtype="bf16",
+                              q_dtype="bf16", budget_pages=200, page_table="random"),
+    "mha_f32_64k_kpt6": dict(B=2, Hq=2, Hkv=2, lens=(65536, 40000), kv_dtype="f32",
+                             q_dtype="f32", budget_pages=130, page_table="random"),
 }
 
 
@@ -299,7 +305,7 @@ def test_step_graph_replays_match_eager(gqa):
         torch.cuda.synchronize()
         assert torch.equal(sel, ref_sel) and torch.equal(num, ref_num), f"replay {rep}: selection"
         assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32)), f"replay {rep}: output"
-        assert sa.step_error_flag(ws) == 0
+        assert_handoff_words_clear(ws, wl.B * wl.Hkv)
         c.step()  # eager work between replays
 
 
@@ -381,3 +387,46 @@ def test_random_workloads(seed):
     kw = _random_case(seed)
     wl = synth.make_custom(**kw, seed=500 + seed, name=f"random{seed}")
     _full_check(wl, f"random{seed}: {kw}")
+
+
+def test_sals_index_query_rounding_adversarial():
+    """The SALS scorer's fixed-point index query against its worst case: every int4
+    code saturated at +-7 (written directly into the index buffers), an identity
+    projection so that the projected query equals q exactly, one component of q at
+    1.0 and the other fifteen just past a half step of a fixed-point grid, with
+    signs chosen so that every token's fifteen rounding errors add up with the same
+    sign.  The scores must stay within the score tolerance of the oracle's
+    double-precision scores.  Emulated on the host, an index query of 22 fractional
+    bits misses the tolerance on the heads placed on its grid (2.3e-6 of the score
+    scale against 2e-6); 26 bits stay at 1.5e-7 on the heads placed on theirs."""
+    Hkv, L = 8, 512
+    wl = synth.make_custom(B=1, Hq=Hkv, Hkv=Hkv, lens=(L,), kv_dtype="bf16", q_dtype="f32",
+                           mode="sals", k_compete=2, seed=77, name="sals-adversarial")
+    rng = np.random.default_rng(77)
+    proj = np.zeros((wl.d, 16), dtype=np.float32)
+    proj[np.arange(16), np.arange(16)] = 1.0
+    sign = rng.choice([-1.0, 1.0], size=(Hkv, 16))
+    k = rng.integers(1000, 8000, size=(Hkv, 16)).astype(np.float64)
+    q = np.zeros((1, Hkv, wl.d), dtype=np.float32)
+    # half the heads just past half steps of a 22-bit grid (2^-21 here), half of a 26-bit
+    # one (2^-25)
+    step = np.where(np.arange(Hkv) < Hkv // 2, 2.0 ** -21, 2.0 ** -25)[:, None]
+    q[0, :, :16] = (sign * (k + 0.5 + 2.0 ** -10) * step).astype(np.float32)
+    q[0, :, 0] = sign[:, 0]  # the largest component, 1.0: the grid exponent is 1
+    nib = np.where(sign > 0, 7, 9).astype(np.uint8)  # +7 / -7 as two's-complement nibbles
+    row = (nib[:, 0::2] | (nib[:, 1::2] << 4)).astype(np.uint8)  # [Hkv, 8]
+    P = wl.num_pages
+    codes = np.broadcast_to(row, (P, 16, Hkv, 8)).copy()
+    scales = synth.f32_to_f16(rng.uniform(4.0, 12.0, size=(P, 16, Hkv)).astype(np.float32))
+    wl.q, wl.proj = q, proj
+    print("[gpu] sals adversarial rounding case", flush=True)
+    c = GpuCase(wl)
+    c.meta = torch.from_numpy(codes).to(c.dev)
+    c.meta_scale = torch.from_numpy(scales.view(np.int16)).to(c.dev)
+    g_sc = c.scores().cpu().numpy()
+    o_sc, o_ab = oracle.sals_scores(q, "f32", codes, scales, proj, wl.page_table, wl.seq_lens,
+                                    Hkv, wl.unit_tokens, wl.lse_scale)
+    check_scores(wl, g_sc, o_sc, o_ab)
+    n = wl.n_units(0)
+    rel = np.abs(g_sc[0, :, :n] - o_sc[0, :, :n]) / np.maximum(np.abs(o_sc[0, :, :n]), o_ab[0, :, :n])
+    print(f"[gpu] sals adversarial: largest error {rel.max():.2e} of the score scale", flush=True)
