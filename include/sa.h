@@ -280,6 +280,29 @@ int sa_sparse_decode_attn(const void *q, int32_t q_dtype, int32_t num_q_heads,
                           const int32_t *num_sel, int32_t max_sel, float softmax_scale, float *out,
                           void *workspace, size_t workspace_bytes, void *stream);
 
+/*
+ * sa_sparse_decode_attn_noalloc - sa_sparse_decode_attn for callers that
+ * cannot allocate device memory (code under HIP graph capture, tight serving
+ * loops, harnesses that forbid allocation): the same computation, kernels and
+ * results (bit for bit), with the split-K partial records in a scratch array
+ * the library holds itself instead of a caller workspace.  The scratch is
+ * 32 MiB of device memory per GPU the library runs on, held until the process
+ * ends; its address is looked up on the first call on each device (make that
+ * first call outside stream capture).  A call whose partial records would
+ * exceed it (sa_attn_workspace_size(...) > 32 MiB, e.g. thousands of lists
+ * with 16-head groups) returns SA_ERR_WORKSPACE_TOO_SMALL before anything is
+ * enqueued.  No call allocates or frees.  Every call on one GPU shares that
+ * GPU's scratch: calls that overlap in time on one GPU (on different streams,
+ * or from different host threads without ordering) race and give undefined
+ * output; calls ordered on one stream are safe.  Arguments, output and errors
+ * otherwise as sa_sparse_decode_attn (SA_ERR_HIP if the scratch cannot be
+ * located).
+ */
+int sa_sparse_decode_attn_noalloc(const void *q, int32_t q_dtype, int32_t num_q_heads,
+                                  const sa_kv_cache *kv, const sa_seqs *seqs, const int32_t *sel,
+                                  const int32_t *num_sel, int32_t max_sel, float softmax_scale,
+                                  float *out, void *stream);
+
 /* Workspace of sa_decode_step.  0 on bad input. */
 size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
                                      const sa_seqs *seqs, const sa_select_cfg *cfg);

@@ -60,7 +60,8 @@ EXPORTS = ["sa_version", "sa_status_string", "sa_meta_bytes", "sa_meta_scale_byt
            "sa_build_page_meta", "sa_append_kv", "sa_max_units", "sa_score_pages", "sa_max_selected",
            "sa_topk_pages", "sa_attn_workspace_size", "sa_sparse_decode_attn",
            "sa_attn_heads_workspace_size", "sa_sparse_decode_attn_heads",
-           "sa_decode_step_workspace_size", "sa_decode_step", "sa_stream_read"]
+           "sa_decode_step_workspace_size", "sa_decode_step", "sa_stream_read",
+           "sa_sparse_decode_attn_noalloc"]
 
 
 def load(path: str = LIB_PATH):
@@ -91,6 +92,7 @@ def load(path: str = LIB_PATH):
         "sa_decode_step_workspace_size": (SZ, [I32, KV, SQ, CF]),
         "sa_decode_step": (ctypes.c_int, [VP, I32, I32, KV, SQ, CF, VP, VP, F, VP, VP, VP, VP, SZ, VP]),
         "sa_stream_read": (ctypes.c_int, [VP, SZ, VP, SZ, VP]),
+        "sa_sparse_decode_attn_noalloc": (ctypes.c_int, [VP, I32, I32, KV, SQ, VP, VP, I32, F, VP, VP]),
     }
     for name, (res, args) in sig.items():
         fn = getattr(lib, name)
@@ -269,6 +271,18 @@ def sa_sparse_decode_attn(q: torch.Tensor, kv: KVCache, seqs: Seqs, sel: Optiona
                                         _ptr(sel), _ptr(num_sel), max_sel, softmax_scale,
                                         _ptr(out), _ptr(workspace), workspace.numel(),
                                         _stream(stream)), "sa_sparse_decode_attn")
+
+
+def sa_sparse_decode_attn_noalloc(q: torch.Tensor, kv: KVCache, seqs: Seqs,
+                                  sel: Optional[torch.Tensor], num_sel: Optional[torch.Tensor],
+                                  softmax_scale: float, out: torch.Tensor, stream=None) -> None:
+    """sa_sparse_decode_attn with the library's own per-GPU scratch instead of a workspace."""
+    max_sel = 0 if sel is None else sel.shape[-1]
+    _check(load().sa_sparse_decode_attn_noalloc(_ptr(q), _dtype_code(q), q.shape[1],
+                                                ctypes.byref(kv.struct()), ctypes.byref(seqs.struct()),
+                                                _ptr(sel), _ptr(num_sel), max_sel, softmax_scale,
+                                                _ptr(out), _stream(stream)),
+           "sa_sparse_decode_attn_noalloc")
 
 
 def sa_sparse_decode_attn_heads(q: torch.Tensor, kv: KVCache, seqs: Seqs, sel: torch.Tensor,

@@ -12,7 +12,30 @@
 
 using namespace sa;
 
+// Scratch of sa_sparse_decode_attn_noalloc: the split-K partial records of one
+// call, in device memory the library holds itself (each GPU the library runs
+// on keeps its own copy until the process ends).  Every record is written by
+// the attention kernel before the merge kernel reads it, so nothing in it has
+// to start at zero.  In host code `scratch` is only a stand-in for the device
+// symbol: the per-device address comes from hipGetSymbolAddress.
+constexpr size_t kNoAllocScratchBytes = (size_t)32 << 20;
+static __device__ __align__(256) float scratch[kNoAllocScratchBytes / sizeof(float)];
+
 namespace {
+
+// This device's copy of scratch, looked up once per device (with it current).
+float* scratch_of_device() {
+  static std::atomic<float*> cache[64];
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return nullptr;
+  float* p = cache[dev].load(std::memory_order_acquire);
+  if (p) return p;
+  void* addr = nullptr;
+  if (hipGetSymbolAddress(&addr, HIP_SYMBOL(scratch)) != hipSuccess || !addr) return nullptr;
+  p = static_cast<float*>(addr);
+  cache[dev].store(p, std::memory_order_release);
+  return p;
+}
 
 constexpr size_t kAlign = 256;
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
@@ -397,6 +420,30 @@ int sa_sparse_decode_attn(const void* q, int32_t q_dtype, int32_t num_q_heads,
                                      s, seqs->page_table, seqs->seq_lens, sel, num_sel,
                                      sel ? max_sel : 0, plan, softmax_scale,
                                      static_cast<float*>(workspace), out,
+                                     static_cast<hipStream_t>(stream)));
+}
+
+int sa_sparse_decode_attn_noalloc(const void* q, int32_t q_dtype, int32_t num_q_heads,
+                                  const sa_kv_cache* kv, const sa_seqs* seqs, const int32_t* sel,
+                                  const int32_t* num_sel, int32_t max_sel, float softmax_scale,
+                                  float* out, void* stream) {
+  int rc;
+  if ((rc = check_kv(kv)) || (rc = check_seqs(seqs))) return rc;
+  if ((rc = check_q(q, q_dtype, num_q_heads, kv->num_kv_heads))) return rc;
+  if (!out) return SA_ERR_INVALID_ARG;
+  if ((sel == nullptr) != (num_sel == nullptr)) return SA_ERR_INVALID_ARG;
+  if (sel && max_sel < 1) return SA_ERR_INVALID_ARG;
+  if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
+  const int list_len = sel ? max_sel : seqs->max_pages;
+  const AttnPlan plan = plan_attention(seqs->batch, num_q_heads, kv->num_kv_heads, list_len,
+                                       sel == nullptr);
+  if (plan.partial_floats * sizeof(float) > kNoAllocScratchBytes) return SA_ERR_WORKSPACE_TOO_SMALL;
+  float* partials = scratch_of_device();
+  if (!partials) return SA_ERR_HIP;
+  const Shapes s = shapes_of(num_q_heads, kv, seqs);
+  return hip_status(launch_attention(kv->dtype, q_dtype, q, kv->k, kv->v, kv->k_scale, kv->v_scale,
+                                     s, seqs->page_table, seqs->seq_lens, sel, num_sel,
+                                     sel ? max_sel : 0, plan, softmax_scale, partials, out,
                                      static_cast<hipStream_t>(stream)));
 }
 

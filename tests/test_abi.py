@@ -244,3 +244,20 @@ def test_stream_read_argument_checks():
     assert lib.sa_stream_read(ctypes.c_void_p(FAKE), 1024, None, 8, None) == sa.SA_ERR_INVALID_ARG
     assert lib.sa_stream_read(ctypes.c_void_p(FAKE), 1024, ctypes.c_void_p(FAKE), 0, None) == sa.SA_ERR_INVALID_ARG
 
+
+def test_noalloc_attention_checks():
+    """sa_sparse_decode_attn_noalloc validates like sa_sparse_decode_attn and rejects a
+    request whose partial records exceed its 32 MiB scratch before any HIP call."""
+    lib = _lib()
+    kv = sa.sa_kv_cache(FAKE, FAKE, None, None, sa.SA_BF16, 4096, 16, 8, 128)
+    big = sa.sa_seqs(FAKE, FAKE, 4096, 16)   # 32768 lists of 16-head groups
+    ok = sa.sa_seqs(FAKE, FAKE, 4, 64)
+    args = lambda seqs, hq, out: (ctypes.c_void_p(FAKE), sa.SA_BF16, hq, ctypes.byref(kv),  # noqa: E731
+                                  ctypes.byref(seqs), ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE), 16,
+                                  0.088, out, None)
+    assert lib.sa_sparse_decode_attn_noalloc(*args(big, 128, ctypes.c_void_p(FAKE))) == \
+        sa.SA_ERR_WORKSPACE_TOO_SMALL
+    assert lib.sa_attn_workspace_size(4096, 128, 8, 16, 16) > 32 << 20
+    assert lib.sa_sparse_decode_attn_noalloc(*args(ok, 24, ctypes.c_void_p(FAKE))) == sa.SA_ERR_UNSUPPORTED
+    assert lib.sa_sparse_decode_attn_noalloc(*args(ok, 16, None)) == sa.SA_ERR_INVALID_ARG
+
