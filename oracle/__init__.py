@@ -21,23 +21,28 @@ from typing import Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "liboracle.so")
+# SA_ORACLE_LIB: load another build of sa_oracle.c (the sanitizer test's instrumented copy)
+_LIB_PATH = os.environ.get("SA_ORACLE_LIB") or os.path.join(_HERE, "liboracle.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 _lib = None
 
 DTYPES = {"f32": 0, "bf16": 1, "i8": 2}
 PAGE = 16
 
 
-def build(verbose: bool = False) -> str:
+def build(verbose: bool = False, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile sa_oracle.c into liboracle.so; sanitize: an AddressSanitizer +
+    UndefinedBehaviorSanitizer build (written to out)."""
     src = os.path.join(_HERE, "sa_oracle.c")
-    tmp = _LIB_PATH + ".tmp"
+    dst = out or _LIB_PATH
+    tmp = dst + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-o", tmp, src, "-lm"]
+           "-fno-fast-math", "-Wall", *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, dst)
+    return dst
 
 
 def _load():

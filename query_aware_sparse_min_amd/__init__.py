@@ -21,7 +21,8 @@ from typing import Optional
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libsa.so")
+# SA_LIB_PATH: load another build of the library (e.g. the host-sanitizer build)
+LIB_PATH = os.environ.get("SA_LIB_PATH") or os.path.join(_HERE, "libsa.so")
 
 SA_OK, SA_ERR_INVALID_ARG, SA_ERR_UNSUPPORTED, SA_ERR_WORKSPACE_TOO_SMALL, SA_ERR_HIP = 0, -1, -2, -3, -4
 SA_F32, SA_BF16, SA_I8 = 0, 1, 2

@@ -21,9 +21,15 @@ FLAGS = ["-O3", "-std=c++17", "-fPIC", f"--offload-arch={ARCH}", "-Wall", "-Wno-
          "-I", os.path.join(ROOT, "include"), "-I", os.path.join(HERE, "csrc")]
 
 
-def _compile(src: str, verbose: bool) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [HIPCC, *FLAGS, "-c", src, "-o", obj]
+# Host-side AddressSanitizer + UndefinedBehaviorSanitizer build: every sanitizer
+# flag is for the host pass only (GPU code is never instrumented).
+HOST_SANITIZE = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined",
+                 "-Xarch_host", "-fno-sanitize-recover=all", "-Xarch_host", "-fno-omit-frame-pointer"]
+
+
+def _compile(src: str, verbose: bool, build_dir: str, extra) -> str:
+    obj = os.path.join(build_dir, os.path.basename(src) + ".o")
+    cmd = [HIPCC, *FLAGS, *extra, "-c", src, "-o", obj]
     if verbose:
         print(" ".join(cmd), flush=True)
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -37,18 +43,23 @@ def _compile(src: str, verbose: bool) -> str:
     return obj
 
 
-def build(verbose: bool = False) -> str:
-    os.makedirs(BUILD_DIR, exist_ok=True)
+def build(verbose: bool = False, out: str = LIB, sanitize_host: bool = False) -> str:
+    """Build libsa.so (in-tree by default); sanitize_host: host code instrumented with
+    AddressSanitizer and UndefinedBehaviorSanitizer (load it with the clang ASan runtime
+    preloaded)."""
+    build_dir = BUILD_DIR + ("_host_asan" if sanitize_host else "")
+    extra = HOST_SANITIZE if sanitize_host else []
+    os.makedirs(build_dir, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(HERE, "csrc", "*.hip")))
     with cf.ThreadPoolExecutor(max_workers=min(8, len(srcs))) as ex:
-        objs = list(ex.map(lambda s: _compile(s, verbose), srcs))
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", "-o", tmp, *objs]
+        objs = list(ex.map(lambda s: _compile(s, verbose, build_dir, extra), srcs))
+    tmp = out + ".tmp"
+    cmd = [HIPCC, "-shared", "-fPIC", f"--offload-arch={ARCH}", *extra, "-o", tmp, *objs]
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.check_call(cmd)
-    os.replace(tmp, LIB)
-    return LIB
+    os.replace(tmp, out)
+    return out
 
 
 if __name__ == "__main__":

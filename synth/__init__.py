@@ -24,7 +24,9 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-_LIB_PATH = os.path.join(_HERE, "libsynth.so")
+# SA_SYNTH_LIB: load another build of synth.c (the sanitizer test's instrumented copy)
+_LIB_PATH = os.environ.get("SA_SYNTH_LIB") or os.path.join(_HERE, "libsynth.so")
+SANITIZE_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer", "-g"]
 _lib = None
 
 PAGE = 16
@@ -36,17 +38,19 @@ T_NEEDLE_PAGE, T_NEEDLE_SLOT, T_LENS, T_PERM, T_OUTLIER, T_PROJ = 7, 8, 9, 10, 1
 T_FRESH_Q = 1000  # + step index
 
 
-def build(verbose: bool = False) -> str:
-    """Compile synth.c into libsynth.so (gcc, OpenMP, no FP contraction)."""
+def build(verbose: bool = False, out: Optional[str] = None, sanitize: bool = False) -> str:
+    """Compile synth.c into libsynth.so (gcc, OpenMP, no FP contraction); sanitize: an
+    AddressSanitizer + UndefinedBehaviorSanitizer build (written to out)."""
     src = os.path.join(_HERE, "synth.c")
-    tmp = _LIB_PATH + ".tmp"
+    dst = out or _LIB_PATH
+    tmp = dst + ".tmp"
     cmd = ["gcc", "-O2", "-std=c11", "-fPIC", "-shared", "-fopenmp", "-ffp-contract=off",
-           "-fno-fast-math", "-Wall", "-o", tmp, src, "-lm"]
+           "-fno-fast-math", "-Wall", *(SANITIZE_FLAGS if sanitize else []), "-o", tmp, src, "-lm"]
     if verbose:
         print(" ".join(cmd))
     subprocess.check_call(cmd)
-    os.replace(tmp, _LIB_PATH)
-    return _LIB_PATH
+    os.replace(tmp, dst)
+    return dst
 
 
 def _load():
