@@ -8,6 +8,7 @@
 #include <atomic>
 
 #include "sa_internal.h"
+#include "sa_post.h"
 #include "sa_step.h"
 
 using namespace sa;
@@ -200,12 +201,15 @@ struct StepLayout {
   bool dense;  // every list keeps all of its units: no scoring needed
   bool fused;  // Quest: one persistent kernel for the whole step
   bool per_head;  // Quest: one selection per query head, attention over the group's union
+  bool post;   // after the scorer: selection, attention and merge in one persistent kernel
   AttnPlan plan;
   StepPlan splan;
+  PostPlan pplan;
   HeadsLayout hl;
 };
 
-StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa_select_cfg* c) {
+StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa_select_cfg* c,
+                       int q_dtype) {
   StepLayout L{};
   L.max_units = max_units_of(s, c);
   L.max_sel = max_sel_of(s, c);
@@ -220,6 +224,11 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
                           L.dense);
   L.splan = plan_step(s->batch, hq, kv->num_kv_heads, s->max_pages, L.max_sel, kPlanCUs);
   const size_t fused_part = (size_t)L.splan.lists * L.splan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2);
+  L.pplan = plan_post(L.splan.lists, hq / kv->num_kv_heads, L.max_sel, kPlanCUs);
+  L.post = !L.dense && !L.per_head && !L.fused && L.pplan.ok &&
+           post_supported(kv->dtype, q_dtype, hq / kv->num_kv_heads, L.max_units);
+  const size_t post_part =
+      L.post ? (size_t)L.pplan.lists * L.pplan.nc * (hq / kv->num_kv_heads) * (kHeadDim + 2) : 0;
   size_t off = 0;
   L.arrive = off;  // the fused kernel's per-list arrival counters
   off = align_up(off + (size_t)L.splan.lists * sizeof(uint32_t));
@@ -230,7 +239,8 @@ StepLayout step_layout(int hq, const sa_kv_cache* kv, const sa_seqs* s, const sa
   L.num_sel = off;
   off = align_up(off + lists * sizeof(int32_t));
   L.partials = off;
-  const size_t pf = L.plan.partial_floats > fused_part ? L.plan.partial_floats : fused_part;
+  size_t pf = L.plan.partial_floats > fused_part ? L.plan.partial_floats : fused_part;
+  if (post_part > pf) pf = post_part;
   off = align_up(off + pf * sizeof(float));
   L.heads = off;
   if (L.per_head) {
@@ -451,7 +461,10 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache* kv,
                                      const sa_seqs* seqs, const sa_select_cfg* cfg) {
   if (check_kv(kv) || check_seqs(seqs) || check_cfg(cfg)) return 0;
   if (!group_ok(num_q_heads, kv->num_kv_heads)) return 0;
-  return step_layout(num_q_heads, kv, seqs, cfg).total;
+  // the larger of the layouts of the two query types the step accepts
+  const size_t a = step_layout(num_q_heads, kv, seqs, cfg, SA_F32).total;
+  const size_t b = step_layout(num_q_heads, kv, seqs, cfg, SA_BF16).total;
+  return a > b ? a : b;
 }
 
 int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache* kv,
@@ -465,7 +478,7 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
   if (!out || !workspace || ((uintptr_t)workspace % kAlign) != 0) return SA_ERR_INVALID_ARG;
   if ((sel == nullptr) != (num_sel == nullptr)) return SA_ERR_INVALID_ARG;
   if (!(softmax_scale == softmax_scale)) return SA_ERR_INVALID_ARG;
-  const StepLayout lay = step_layout(num_q_heads, kv, seqs, cfg);
+  const StepLayout lay = step_layout(num_q_heads, kv, seqs, cfg, q_dtype);
   if (lay.per_head && seqs->max_pages > kUnionPages) return SA_ERR_UNSUPPORTED;
   if (workspace_bytes < lay.total) return SA_ERR_WORKSPACE_TOO_SMALL;
   if (!lay.dense && cfg->mode != SA_MODE_PROBE) {
@@ -560,6 +573,37 @@ int sa_decode_step(const void* q, int32_t q_dtype, int32_t num_q_heads, const sa
                                       cfg->proj, s, seqs->page_table, seqs->seq_lens,
                                       cfg->unit_tokens, cfg->lse_scale, scores, lay.max_units, st));
   if (rc) return rc;
+  if (lay.post) {
+    PostArgs A{};
+    A.q = q;
+    A.k = kv->k;
+    A.v = kv->v;
+    A.ks = kv->k_scale;
+    A.vs = kv->v_scale;
+    A.pt = seqs->page_table;
+    A.lens = seqs->seq_lens;
+    A.hkv = kv->num_kv_heads;
+    A.num_pages = kv->num_pages;
+    A.max_pages = seqs->max_pages;
+    A.unit_tokens = cfg->unit_tokens;
+    A.max_units = lay.max_units;
+    A.k_compete = cfg->k_compete;
+    A.n_head = cfg->n_head_forced;
+    A.n_tail = cfg->n_tail_forced;
+    A.scale_log2 = softmax_scale * kLog2e;
+    A.scores = scores;
+    A.sel = sel;
+    A.num_sel = num_sel;
+    A.max_sel = lay.max_sel;
+    A.partials = partials;
+    A.out = out;
+    A.arrive = reinterpret_cast<uint32_t*>(ws + lay.arrive);
+    PostPlan P = lay.pplan;
+    const int cus = device_cus(), cap = step_wg_cap();
+    P.grid = P.n_tasks < cus ? P.n_tasks : cus;
+    if (cap > 0 && cap < P.grid) P.grid = cap;
+    return hip_status(launch_post_score(kv->dtype, num_q_heads / kv->num_kv_heads, A, P, st));
+  }
   rc = hip_status(launch_topk(scores, lay.max_units, s, seqs->seq_lens, cfg->unit_tokens,
                               cfg->k_compete, cfg->n_head_forced, cfg->n_tail_forced, sel_buf,
                               num_buf, lay.max_sel, st));

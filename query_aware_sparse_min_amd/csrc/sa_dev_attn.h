@@ -375,7 +375,10 @@ __device__ __forceinline__ void static_for(F&& f) {
 // row, and P V stays on the vector ALUs in fp32 (no bf16 rounding of weights).
 // int8 K / V: the codes enter the MFMA exactly; the per-token scales multiply
 // the scores and the weights.  Partials as attend_range.
-template <int KT, int G, int NW = 4>
+// PW: pages each wave loads per iteration, all in flight before any is used.
+// rlst / COH: as attend_range (pages already resolved to (physical page << 4) |
+// (valid tokens - 1), read from LDS; partial records stored device-coherently).
+template <int KT, int G, int NW = 4, int PW = 1, bool COH = false>
 __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
                                                   const void* __restrict__ k,
                                                   const void* __restrict__ v,
@@ -386,7 +389,8 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
                                                   const int32_t* lst, int j0, int j1,
                                                   float scale_log2, float* __restrict__ part,
                                                   AttnSmem<G, NW>& sm, int jcap = -1,
-                                                  bool masked = false) {
+                                                  bool masked = false,
+                                                  const int32_t* rlst = nullptr) {
   static_assert(G >= 1 && G <= 16, "one MFMA column per query head");
   static_assert(KT == SA_BF16 || KT == SA_I8, "K enters the MFMA as bf16");
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -416,67 +420,73 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 #pragma unroll
     for (int e = 0; e < 8; ++e) acc[g][e] = 0.0f;
 
-  const WavePages<false, NW> page_of(pt_row, lst, nullptr, j0, j1, L, num_pages, jcap, masked);
-  for (int jb = j0 + wave; jb < j1; jb += NW) {
-    const PageRef pg = page_of(jb);
-    const size_t ppl = pg.pp >= 0 ? (size_t)pg.pp : 0;  // empty slot: load page 0, result unused
-    KOp8<KT> kr[4];
-    {
+  const WavePages<false, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages, jcap, masked);
+  for (int jb = j0 + wave; jb < j1; jb += NW * PW) {
+    PageRef pg[PW];
+    KOp8<KT> kr[PW][4];
+    Raw8<KT> vr[PW][4];
+    float ksc[PW][4], vsc[PW][4];
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      pg[u] = page_of(jb + NW * u);
+      const size_t ppl = pg[u].pp >= 0 ? (size_t)pg[u].pp : 0;  // empty slot: load page 0, result unused
       const size_t row = (ppl * kPage + tok_a) * hkv + h;
 #pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kr[kk].load(k, row * kHeadDim + 32 * qg + 8 * kk);
-    }
-    Raw8<KT> vr[4];
-    float ksc[4], vsc[4];
-#pragma unroll
-    for (int it = 0; it < 4; ++it) {
-      const size_t tv = (ppl * kPage + 4 * it + r) * hkv + h;
-      vr[it].load(v, tv * kHeadDim + 8 * c);
-      if constexpr (KT == SA_I8) {
-        ksc[it] = f16_to_f32(ks[(ppl * kPage + 4 * it + qg) * hkv + h]);
-        vsc[it] = f16_to_f32(vs[tv]);
-      } else {
-        ksc[it] = vsc[it] = 1.0f;
-      }
-    }
-    // every load of the page is issued before any of them is used
-    __builtin_amdgcn_sched_barrier(0);
-    f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
-#pragma unroll
-    for (int kk = 0; kk < 4; ++kk) z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[kk].get(), qb[kk], z, 0, 0, 0);
-
-    const bool live = pg.pp >= 0 && n < G && ((pg.mask >> n) & 1u);
-    float zz[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)  // token 4 i + qg
-      zz[i] = (live && 4 * i + qg < pg.nv) ? z[i] * (scale_log2 * ksc[i]) : -INFINITY;
-    float pm = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
-    pm = pair32_max(pair16_max(pm));  // over the page's 16 tokens, for head n
-    const float mn = fmaxf(mrun, pm);
-    const bool none = mn == -INFINITY;
-    const float alpha = none ? 1.0f : exp2f(mrun - mn);
-    float p[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) p[i] = none ? 0.0f : exp2f(zz[i] - mn);
-    lpart = fmaf(lpart, alpha, (p[0] + p[1]) + (p[2] + p[3]));
-    mrun = mn;
-
-    static_for<0, G>([&](auto gc) {
-      constexpr int g = decltype(gc)::value;
-      const float ag = row_bcast<g>(alpha);
-      float pw[4];
-#pragma unroll
-      for (int it = 0; it < 4; ++it) pw[it] = row_bcast<g>(p[it]) * vsc[it];
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+      for (int kk = 0; kk < 4; ++kk) kr[u][kk].load(k, row * kHeadDim + 32 * qg + 8 * kk);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
-        float vx[8];
-        vr[it].get(vx);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[it], vx[e], acc[g][e]);
+        const size_t tv = (ppl * kPage + 4 * it + r) * hkv + h;
+        vr[u][it].load(v, tv * kHeadDim + 8 * c);
+        if constexpr (KT == SA_I8) {
+          ksc[u][it] = f16_to_f32(ks[(ppl * kPage + 4 * it + qg) * hkv + h]);
+          vsc[u][it] = f16_to_f32(vs[tv]);
+        } else {
+          ksc[u][it] = vsc[u][it] = 1.0f;
+        }
       }
-    });
+    }
+    // every load of the iteration is issued before any of them is used
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int u = 0; u < PW; ++u) {
+      f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
+#pragma unroll
+      for (int kk = 0; kk < 4; ++kk)
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[u][kk].get(), qb[kk], z, 0, 0, 0);
+
+      const bool live = pg[u].pp >= 0 && n < G && ((pg[u].mask >> n) & 1u);
+      float zz[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i)  // token 4 i + qg
+        zz[i] = (live && 4 * i + qg < pg[u].nv) ? z[i] * (scale_log2 * ksc[u][i]) : -INFINITY;
+      float pm = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
+      pm = pair32_max(pair16_max(pm));  // over the page's 16 tokens, for head n
+      const float mn = fmaxf(mrun, pm);
+      const bool none = mn == -INFINITY;
+      const float alpha = none ? 1.0f : exp2f(mrun - mn);
+      float p[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p[i] = none ? 0.0f : exp2f(zz[i] - mn);
+      lpart = fmaf(lpart, alpha, (p[0] + p[1]) + (p[2] + p[3]));
+      mrun = mn;
+
+      static_for<0, G>([&](auto gc) {
+        constexpr int g = decltype(gc)::value;
+        const float ag = row_bcast<g>(alpha);
+        float pw[4];
+#pragma unroll
+        for (int it = 0; it < 4; ++it) pw[it] = row_bcast<g>(p[it]) * vsc[u][it];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
+#pragma unroll
+        for (int it = 0; it < 4; ++it) {
+          float vx[8];
+          vr[u][it].get(vx);
+#pragma unroll
+          for (int e = 0; e < 8; ++e) acc[g][e] = fmaf(pw[it], vx[e], acc[g][e]);
+        }
+      });
+    }
   }
 
   // fold the four token rows of each wave, then the NW waves
@@ -495,7 +505,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 #pragma unroll
       for (int e = 0; e < 8; ++e) sm.acc[wave][g][8 * c + e] = acc[g][e];
   }
-  put_partials<G, NW, false>(sm, part);
+  put_partials<G, NW, COH>(sm, part);
 }
 
 // Merge ns partial records part[ns][G][kPartStride] of one list into

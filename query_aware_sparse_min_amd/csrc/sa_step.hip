@@ -6,18 +6,19 @@
 //
 // Every list (batch, kv-head) is cut into nc chunks of consecutive logical
 // pages; one task per chunk does, in one workgroup:
-//   1. score its pages (Quest bound) and store their order keys, keeping the
-//      chunk's physical page numbers in LDS;
+//   1. score its pages (Quest bound) and store their order keys, with the
+//      list's page-table row fetched alongside into LDS;
 //   2. run the exact top-K of the whole list from all of its keys -- every
-//      chunk of the list computes the same selection -- and keep only the
-//      selected pages of its own chunk (writing their entries of the optional
-//      page list at their global ranks);
+//      chunk of the list computes the same selection, with each kept page's
+//      rank -- and take the kept pages of ranks [c K / nc, (c + 1) K / nc)
+//      (K kept pages), an equal share wherever they lie in the list, resolved
+//      through the row in LDS (writing their entries of the optional page
+//      list at their ranks);
 //   3. attend to those pages (online softmax) and store one partial record;
 //   4. count itself done on the list's arrival counter; the chunk that
 //      arrives last merges the list's nc partial records into out and returns
 //      the list's keys and counter to 0.
-// So only the scores cross between workgroups before the attention, and the
-// page table is read once per page.
+// So only the scores cross between workgroups before the attention.
 //
 // No workgroup ever waits for another one, so the kernel is correct whatever
 // subset of its grid is resident at a time:
@@ -76,23 +77,22 @@ struct StepHelp {
 };
 
 // KPT: top-K keys per thread in registers (lists of up to 768 * KPT pages).
-template <int KT, int QT, int G, int KPT>
+// PW: pages each wave of the attention loads at once.
+template <int KT, int QT, int G, int KPT, int PW>
 __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A, StepPlan P) {
   __shared__ StepSmem<G> sm;
-  __shared__ int32_t s_pp[kStepMaxChunk];    // physical page of each chunk page, or -1
-  // chunk page kept by the selection: (physical << 4) | (valid - 1), else -1
-  __shared__ int32_t s_kept[kStepMaxChunk];
-  __shared__ int32_t s_list[kStepMaxChunk];  // kept pages: (physical << 4) | (valid - 1)
+  __shared__ int32_t s_pt[kStepThreads * KPT];   // the list's page-table row
+  // this chunk's share of the kept pages: (physical << 4) | (valid - 1), or -1
+  __shared__ int32_t s_list[kStepMaxChunk];
   __shared__ uint32_t s_help[kStepMaxPages / kChunkGrain / 32];  // chunks whose keys are missing
-  __shared__ int s_cnt, s_last;
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  __shared__ int s_last;
+  const int tid = threadIdx.x;
   const int hq = A.hkv * G;
 
   for (int t = blockIdx.x; t < P.n_tasks; t += gridDim.x) {
     const int i = t / P.nc, c = t % P.nc;
     const int b = i / A.hkv, h = i % A.hkv;
     const int32_t* pt_row = A.pt + (size_t)b * A.max_pages;
-    const int c0 = c * P.chunk_pages;
     float* sc_row = A.scores + (size_t)i * A.max_pages;
 
     // scores of chunk cc stored as order keys, IT page pairs per lane and pass;
@@ -100,74 +100,64 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     // loads need not wait for the sequence length.  A page's key does not
     // depend on IT (sixteen lanes of one row reduce it in a fixed order).
     // Returns the list's page count.
-    auto score_chunk = [&](auto it_c, int cc, int32_t* pp_out) {
+    auto score_chunk = [&](auto it_c, int cc) {
       constexpr int IT = decltype(it_c)::value, kPass = 4 * kStepWaves * IT;
       const int a0 = cc * P.chunk_pages, a1 = min(a0 + P.chunk_pages, A.max_pages);
       int nv = 0;
       for (int p0 = a0; p0 < a1; p0 += kPass)
         nv = quest_score_range<KT, QT, G, IT, true, kStepWaves, true>(
             A.q, A.meta, A.num_pages, A.hkv, b, h, pt_row, p0, min(p0 + kPass, a1), A.lens + b,
-            A.max_pages, sc_row, pp_out ? pp_out + (p0 - a0) : nullptr);
+            A.max_pages, sc_row);
       return nv;
     };
     // the help path scores with one page pair per lane: fewer registers live
     // beside the selection's
-    auto help_chunk = [&](int cc) { score_chunk(std::integral_constant<int, 1>{}, cc, nullptr); };
+    auto help_chunk = [&](int cc) { score_chunk(std::integral_constant<int, 1>{}, cc); };
 
-    // 1. scores of the chunk
-    int n = score_chunk(std::integral_constant<int, kScoreIT>{}, c, s_pp);
+    // 1. scores of the chunk; the list's page-table row (any kept page of the
+    // list may fall to this chunk) goes out with the score loads and is parked
+    // in LDS.  (fp32 metadata: half the page pairs per pass, for the register
+    // budget.)
+    int32_t ptv[KPT];
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) ptv[r] = pt_row[min(tid + kStepThreads * r, A.max_pages - 1)];
+    int n = score_chunk(std::integral_constant<int, KT == SA_F32 ? kScoreIT / 2 : kScoreIT>{}, c);
     const int L = clamp_len(A.lens[b], A.max_pages);
-    if (c0 >= A.max_pages) n = (L + kPage - 1) / kPage;
-    const int c1 = min(c0 + P.chunk_pages, n);  // c1 <= c0: an empty chunk
-    for (int j = tid; j < P.chunk_pages; j += kStepThreads) s_kept[j] = -1;
+    if (c * P.chunk_pages >= A.max_pages) n = (L + kPage - 1) / kPage;
+#pragma unroll
+    for (int r = 0; r < KPT; ++r) s_pt[tid + kStepThreads * r] = ptv[r];
     for (int j = tid; j < (int)(sizeof(s_help) / sizeof(s_help[0])); j += kStepThreads) s_help[j] = 0u;
-    __syncthreads();  // the clears (and s_pp) before the selection marks kept pages
+    __syncthreads();  // s_pt and the clears before the selection
 
     // 2. the list's selection (its keys re-read until all have arrived, or
-    // scored here); keep this chunk's part
+    // scored here).  The kept pages are shared out by rank: chunk c attends to
+    // the kept pages of ranks [lo, hi), an equal share whatever their place in
+    // the list, resolved through the page-table row in LDS.
+    const int kept = n <= A.n_head + A.n_tail + A.k_compete ? n : A.n_head + A.k_compete + A.n_tail;
+    const int lo = (int)((long)c * kept / P.nc), hi = (int)((long)(c + 1) * kept / P.nc);
     int32_t* sel_row = A.sel ? A.sel + (size_t)i * A.max_sel : nullptr;
     const StepHelp<decltype(help_chunk)> help{s_help, P.chunk_pages, P.nc, help_chunk};
     topk_core<kStepThreads, KPT, true, true>(sc_row, n, A.k_compete, A.n_head, A.n_tail, sm.topk,
                                              [&](int rank, int u) {
-                                               if (u >= c0 && u < c1) {
-                                                 const int pp = s_pp[u - c0];
-                                                 if (pp >= 0) s_kept[u - c0] = (pp << 4) | (min(kPage, L - u * kPage) - 1);
+                                               if (rank >= lo && rank < hi) {
+                                                 const int pp = s_pt[u];
+                                                 s_list[rank - lo] = (pp >= 0 && pp < A.num_pages)
+                                                     ? (pp << 4) | (min(kPage, L - u * kPage) - 1) : -1;
                                                  if (sel_row && rank < A.max_sel) sel_row[rank] = u;
                                                }
-                                             }, sel_row != nullptr, help);
+                                             }, true, help);
     if (sel_row && c == 0) {  // count and padding of the optional page list
-      const int cnt = min(min(n, A.n_head + A.k_compete + A.n_tail), A.max_sel);
+      const int cnt = min(kept, A.max_sel);
       for (int j = cnt + tid; j < A.max_sel; j += kStepThreads) sel_row[j] = -1;
       if (tid == 0) A.num_sel[i] = cnt;
     }
-    __syncthreads();
-    if (wave == 0) {  // kept pages of the chunk, ascending (four reads in flight per round)
-      const int nch = c1 - c0;
-      int cnt = 0;
-      for (int base = 0; base < nch; base += 256) {
-        int32_t v[4];
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int j = base + 64 * q + lane;
-          const int32_t x = s_kept[min(j, kStepMaxChunk - 1)];
-          v[q] = j < nch ? x : -1;
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const uint64_t bal = __ballot(v[q] >= 0);
-          if (v[q] >= 0) s_list[cnt + __popcll(bal & ((1ull << lane) - 1ull))] = v[q];
-          cnt += __popcll(bal);
-        }
-      }
-      if (lane == 0) s_cnt = cnt;
-    }
-    __syncthreads();
+    __syncthreads();  // s_list complete
 
-    // 3. attention over the chunk's kept pages
+    // 3. attention over the chunk's share of the kept pages
     float* part_list = A.partials + (size_t)i * P.nc * G * kPartStride;
-    attend_range<KT, QT, G, 1, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b, h,
-                                                 pt_row, L, nullptr, 0, s_cnt, A.scale_log2,
-                                                 part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
+    attend_range<KT, QT, G, PW, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b,
+                                                  h, pt_row, L, nullptr, 0, hi - lo, A.scale_log2,
+                                                  part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
     // 4. arrival: every store of this task has completed before the count
     stores_done();
     __syncthreads();
@@ -191,9 +181,12 @@ constexpr int kKptHi = (kStepMaxPages + kStepThreads - 1) / kStepThreads;
 
 typedef void (*StepKernel)(StepArgs, StepPlan);
 
+// two pages in flight per wave where the K/V rows are 16-bit (bf16): one round
+// of loads covers a chunk's usual share; fp32 rows keep one (register budget)
 template <int KT, int QT>
 StepKernel step_kernel_of(int kpt) {
-  return kpt <= kKptLo ? quest_step_kernel<KT, QT, 1, kKptLo> : quest_step_kernel<KT, QT, 1, kKptHi>;
+  constexpr int PW = KT == SA_BF16 ? 2 : 1;
+  return kpt <= kKptLo ? quest_step_kernel<KT, QT, 1, kKptLo, PW> : quest_step_kernel<KT, QT, 1, kKptHi, PW>;
 }
 
 StepKernel kernel_of(int kv_dtype, int q_dtype, int kpt) {

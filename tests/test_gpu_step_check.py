@@ -12,6 +12,10 @@
   resident while its first chunk runs, so that chunk scores the other chunks'
   pages itself after its bounded wait.  The output, the page lists and the
   cleared workspace must equal those of the full grid bit for bit.
+* The same holds for the persistent selection + attention + merge kernel that
+  follows a separate scorer (SALS on an int8 cache, Quest with GQA groups):
+  capped at one or a few workgroups, output and page lists are bit-identical
+  and the arrival counters return to zero.
 """
 import os
 
@@ -43,7 +47,7 @@ def _run(c, wl, ws, want_sel=True):
     ms = sa.sa_max_selected(c.seqs, c.cfg)
     sel = torch.full((wl.B, wl.Hkv, ms), -7, dtype=torch.int32, device=c.dev) if want_sel else None
     num = torch.full((wl.B, wl.Hkv), -7, dtype=torch.int32, device=c.dev) if want_sel else None
-    sa.sa_decode_step(c.d.q, c.kv, c.seqs, c.cfg, c.meta, None, wl.softmax_scale, out, ws, sel, num)
+    sa.sa_decode_step(c.d.q, c.kv, c.seqs, c.cfg, c.meta, c.meta_scale, wl.softmax_scale, out, ws, sel, num)
     torch.cuda.synchronize()
     return out, sel, num
 
@@ -78,3 +82,28 @@ def test_fused_step_with_few_resident_workgroups(grid):
             assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32))
     finally:
         del os.environ["SA_STEP_MAX_WORKGROUPS"]
+
+
+@pytest.mark.parametrize("grid", [1, 5])
+@pytest.mark.parametrize("kind", ["sals_i8", "gqa4_bf16", "gqa16_bf16", "probe_gqa2"])
+def test_post_score_kernel_with_few_resident_workgroups(kind, grid):
+    kw = {"sals_i8": dict(B=2, Hq=8, Hkv=2, lens=(5000, 1300), kv_dtype="i8", mode="sals", k_compete=9),
+          "gqa4_bf16": dict(B=3, Hq=16, Hkv=4, lens=(4000, 777, 2500), kv_dtype="bf16", budget_pages=40),
+          "gqa16_bf16": dict(B=1, Hq=32, Hkv=2, lens=(3000,), kv_dtype="bf16", budget_pages=24),
+          "probe_gqa2": dict(B=2, Hq=8, Hkv=4, lens=(2000, 900), kv_dtype="bf16", mode="probe",
+                             k_compete=10)}[kind]
+    wl = synth.make_custom(q_dtype="bf16", page_table="random", seed=72, **kw)
+    c = GpuCase(wl)
+    c.build_meta()
+    print(f"[gpu] post-score kernel {kind} on {grid} workgroups", flush=True)
+    ws = sa.alloc_workspace(sa.sa_decode_step_workspace_size(wl.Hq, c.kv, c.seqs, c.cfg), c.dev)
+    ref_out, ref_sel, ref_num = _run(c, wl, ws)
+    os.environ["SA_STEP_MAX_WORKGROUPS"] = str(grid)
+    try:
+        out, sel, num = _run(c, wl, ws)
+    finally:
+        del os.environ["SA_STEP_MAX_WORKGROUPS"]
+    assert int(torch.count_nonzero(ws[:4 * wl.B * wl.Hkv])) == 0, "arrival counters left behind"
+    assert torch.equal(sel, ref_sel) and torch.equal(num, ref_num)
+    assert torch.equal(out.view(torch.int32), ref_out.view(torch.int32))
+
