@@ -63,32 +63,50 @@ def parse():
                          "decode-time append on config 2 / 4), e.g. --configs 1,3,3h,4,5,5d,2p,2a,4a")
     ap.add_argument("--parse-pmc", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"),
                     help="write the HBM traffic record from two rocprofv3 --pmc outputs")
+    ap.add_argument("--pmc-kernels", default="",
+                    help="with --parse-pmc: print scaled bytes per launch of these kernels "
+                         "(comma-separated name parts) instead of writing the step record")
     return ap.parse_args()
 
 
-def parse_pmc(fetch_csv, write_csv):
-    """HBM bytes per step-kernel launch from rocprofv3 counter files (FETCH_SIZE,
+def parse_pmc(fetch_csv, write_csv, kernels=""):
+    """HBM bytes per kernel launch from rocprofv3 counter files (FETCH_SIZE,
     WRITE_SIZE in KiB per dispatch), each scaled by what the same counter reads
-    for the plain copy of CALIB_BYTES that the counter run also launches."""
+    for the plain copy of CALIB_BYTES that the counter run also launches.  Without
+    `kernels` this writes the record of the fused step kernel; with a list of kernel
+    names it prints one line per kernel."""
     import csv
-    import json
 
-    def per_kernel(path, counter):
-        """(step-kernel values, value of the last copy dispatch) in bytes."""
+    def per_kernel(path, counter, name):
+        """(values of kernels whose name contains `name`, last copy dispatch) in bytes."""
         step, copies = [], []
         with open(path) as fh:
             for r in csv.DictReader(fh):
                 if r.get("Counter_Name") != counter:
                     continue
                 v = float(r["Counter_Value"]) * 1024.0
-                if STEP_KERNEL in r["Kernel_Name"]:
+                if name in r["Kernel_Name"]:
                     step.append(v)
                 elif "copy" in r["Kernel_Name"].lower():
                     copies.append((int(r["Dispatch_Id"]), v))
         return step, max(copies)[1]  # the calibration copy is the last copy dispatched
 
-    fs, fc = per_kernel(fetch_csv, "FETCH_SIZE")
-    ws, wc = per_kernel(write_csv, "WRITE_SIZE")
+    if kernels:
+        for name in kernels.split(","):
+            fs, fc = per_kernel(fetch_csv, "FETCH_SIZE", name)
+            ws, wc = per_kernel(write_csv, "WRITE_SIZE", name)
+            if not fs or not ws:
+                print(json.dumps({"kernel": name, "dispatches": 0}))
+                continue
+            fk, wk = sum(fs) / len(fs), sum(ws) / len(ws)
+            print(json.dumps({"kernel": name, "dispatches": len(fs),
+                              "fetch_bytes_raw": round(fk), "write_bytes_raw": round(wk),
+                              "fetch_scale": CALIB_BYTES / fc, "write_scale": CALIB_BYTES / wc,
+                              "fetch_bytes": round(fk * CALIB_BYTES / fc),
+                              "write_bytes": round(wk * CALIB_BYTES / wc)}))
+        return
+    fs, fc = per_kernel(fetch_csv, "FETCH_SIZE", STEP_KERNEL)
+    ws, wc = per_kernel(write_csv, "WRITE_SIZE", STEP_KERNEL)
     fk, wk = sum(fs) / len(fs), sum(ws) / len(ws)
     rec = {"kernel": STEP_KERNEL, "kernel_src_sha": kernel_source_hash(),
            "fetch_bytes_raw": round(fk), "write_bytes_raw": round(wk),
@@ -116,7 +134,7 @@ def load_traffic():
 def main():
     args = parse()
     if args.parse_pmc:
-        parse_pmc(*args.parse_pmc)
+        parse_pmc(*args.parse_pmc, kernels=args.pmc_kernels)
         return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
@@ -391,6 +409,27 @@ def config_line(name, args):
     def step(i):
         kv, meta, mscale = copies[i % R]
         sa.sa_decode_step(qs[i % NQ], kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws)
+
+    if args.pmc_run:  # eager steps on rotated copies, then the calibration copy
+        for i in range(args.warmup + 4):
+            step(i)
+        torch.cuda.synchronize()
+        n_lists = wl.Hq if per_head else wl.Hkv
+        num = torch.empty((wl.B, n_lists), dtype=torch.int32, device=dev)
+        sel = torch.empty((wl.B, n_lists, ms), dtype=torch.int32, device=dev)
+        kv, meta, mscale = copies[0]
+        sa.sa_decode_step(qs[0], kv, seqs, cfg, meta, mscale, wl.softmax_scale, out, ws, sel, num)
+        num_np = num.cpu().numpy()
+        src = torch.empty(CALIB_BYTES // 4, dtype=torch.float32, device=dev).fill_(1.0)
+        dst = torch.empty_like(src)
+        torch.cuda.synchronize()
+        dst.copy_(src)  # the last copy dispatched: the calibration
+        torch.cuda.synchronize()
+        if not per_head:
+            print(json.dumps({"workload": wl.name, "bytes": {k2: int(v2) for k2, v2 in
+                                                             synth.step_bytes(wl, num_np).items()}}))
+        print("pmc run done", flush=True)
+        return
 
     def graph_us(fn, n):
         for i in range(min(n, args.warmup)):
