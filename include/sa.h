@@ -323,7 +323,12 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  * workgroups hand score keys and partial records to each other through the
  * workspace; no workgroup ever waits for another, so the result does not
  * depend on how many of them are resident at a time (a build that uses
- * scratch memory runs the separate kernels instead; same results).
+ * scratch memory runs the separate kernels instead; same results).  Other
+ * steps with a bf16 query, bf16 or int8 K/V and lists short enough for the
+ * selection's register keys (sa_max_units up to 4 per selection thread) run
+ * the scorer and then one persistent kernel for the top-K, the attention and
+ * the merge, whose chunk workgroups hand partial records to the last-arriving
+ * one the same way; the rest run the separate kernels.
  * Workspace protocol of every sa_decode_step call:
  *  - the workspace must be zero-filled before its first use;
  *  - every call leaves its hand-off words (per-list arrival counters and score
@@ -333,7 +338,7 @@ size_t sa_decode_step_workspace_size(int32_t num_q_heads, const sa_kv_cache *kv,
  *  - one workspace serves one call at a time: calls that share it must be
  *    ordered on one stream.
  * The environment variable SA_STEP_MAX_WORKGROUPS (a positive integer, read
- * at every call) caps the persistent kernel's workgroups, e.g. to leave
+ * at every call) caps the persistent kernels' workgroups, e.g. to leave
  * compute units to other work; the result is the same bit for bit.
  */
 int sa_decode_step(const void *q, int32_t q_dtype, int32_t num_q_heads, const sa_kv_cache *kv,
