@@ -55,7 +55,7 @@ constexpr uint64_t kKeyWaitTicks = 2000;
 template <int NT>
 struct TopkSmem {
   alignas(16) uint32_t hist[3][kTopkBins];
-  uint32_t wmin[NT / 64], wmax[NT / 64];
+  uint32_t wmin[NT / 64], wmax[NT / 64], wmiss[NT / 64];
   uint32_t wa[NT / 64], wb[NT / 64];
   int last_kept;
 };
@@ -69,7 +69,7 @@ struct TopkSmem {
 // order_key() words written by other workgroups, 0 while not yet written; such
 // words are re-read for up to kKeyWaitTicks, and any still missing then are
 // produced through help (so the call never depends on another workgroup
-// being resident).  All NT threads call; sm is free again on return once the
+// being resident).  With k = 0 the keys are not needed and nothing is waited for.  All NT threads call; sm is free again on return once the
 // caller has synchronised.
 template <int NT, int KPT, bool COH, bool KEYS = false, typename Keep, typename Help = NoHelp>
 __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, int k, int n_head,
@@ -93,13 +93,14 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   // in-range indices so that they are all in flight together; out-of-run
   // values are discarded afterwards.
   uint32_t key[KPT > 0 ? KPT : 1];
+  const uint32_t* mk = reinterpret_cast<const uint32_t*>(sc) + n_head;  // KEYS: the order-key words
+  bool missing = false;  // KEYS: a key of this thread's run has not arrived
   if constexpr (KEYS) {
-    const uint32_t* mk = reinterpret_cast<const uint32_t*>(sc) + n_head;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = ld_x<true>(mk + min(r0 + j, m - 1));
-    bool missing = false;
 #pragma unroll
     for (int j = 0; j < KPT; ++j) missing |= j < cnt_t && key[j] == 0u;
+    if (k == 0) missing = false;  // no competing unit is kept: the keys are not needed
     if (missing) {  // stores not yet landed: re-read those words, for a bounded time
       const uint64_t t_end = __builtin_amdgcn_s_memrealtime() + kKeyWaitTicks;
       while (missing && __builtin_amdgcn_s_memrealtime() < t_end) {
@@ -114,17 +115,8 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
         }
       }
     }
-    if (__syncthreads_or(missing ? 1 : 0)) {  // still missing: their units are produced here
-#pragma unroll
-      for (int j = 0; j < KPT; ++j)
-        if (j < cnt_t && key[j] == 0u) help.mark(n_head + r0 + j);
-      __syncthreads();
-      help.run();
-      __syncthreads();
-      // every key is read again, so that none is held in registers while help runs
-#pragma unroll
-      for (int j = 0; j < KPT; ++j) key[j] = ld_x<true>(mk + min(r0 + j, m - 1));
-    }
+    // keys still missing are produced through help once the block knows of
+    // them (at the barrier of the key bounds below)
 #pragma unroll
     for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? key[j] : 0u;
   } else if constexpr (KPT > 0) {
@@ -154,14 +146,44 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   // them); rem of them are kept, every key above is kept
   uint32_t dm = 0xFFFFFFFFu, tval = 0xFFFFFFFFu, rem = 0, cbin = 0;
   if (k > 0) {
-    uint32_t kmin = 0xFFFFFFFFu, kmax = 0u;
-    for_keys([&](int, uint32_t x) { kmin = min(kmin, x); kmax = max(kmax, x); });
-    kmin = wave_min_u32(kmin);
-    kmax = wave_max_u32(kmax);
-    if (lane == 0) { sm.wmin[wave] = kmin; sm.wmax[wave] = kmax; }
-    __syncthreads();  // also orders the histogram clears before the first pass
+    // block min/max of the keys; with KEYS the same barrier tells every
+    // thread whether any key of the list is still missing
+    uint32_t kmin, kmax;
+    auto bounds = [&]() -> bool {
+      kmin = 0xFFFFFFFFu;
+      kmax = 0u;
+      for_keys([&](int, uint32_t x) { kmin = min(kmin, x); kmax = max(kmax, x); });
+      kmin = wave_min_u32(kmin);
+      kmax = wave_max_u32(kmax);
+      const uint32_t miss = (KEYS && __ballot(missing ? 1 : 0) != 0ull) ? 1u : 0u;
+      if (lane == 0) { sm.wmin[wave] = kmin; sm.wmax[wave] = kmax; sm.wmiss[wave] = miss; }
+      __syncthreads();  // also orders the histogram clears before the first pass
+      uint32_t any = 0u;
 #pragma unroll
-    for (int w = 0; w < NW; ++w) { kmin = min(kmin, sm.wmin[w]); kmax = max(kmax, sm.wmax[w]); }
+      for (int w = 0; w < NW; ++w) {
+        kmin = min(kmin, sm.wmin[w]);
+        kmax = max(kmax, sm.wmax[w]);
+        any |= sm.wmiss[w];
+      }
+      return any != 0u;
+    };
+    if (bounds()) {  // KEYS only: missing keys; their units are produced here
+      if constexpr (KEYS) {
+#pragma unroll
+        for (int j = 0; j < KPT; ++j)
+          if (j < cnt_t && key[j] == 0u) help.mark(n_head + r0 + j);
+        __syncthreads();
+        help.run();
+        __syncthreads();
+        // every key is read again, so that none is held in registers while help runs
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = ld_x<true>(mk + min(r0 + j, m - 1));
+#pragma unroll
+        for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? key[j] : 0u;
+        missing = false;
+        (void)bounds();
+      }
+    }
     rem = (uint32_t)k;
     const uint32_t diff = kmin ^ kmax;
     tval = kmax;
