@@ -53,7 +53,6 @@ template <int G>
 union StepSmem {
   TopkSmem<kStepThreads> topk;
   AttnSmem<G, kStepWaves> attn;
-  float merge[3 * kStepThreads];
 };
 
 // Keys of a list that have not arrived in time: the chunks that hold them are
@@ -80,12 +79,12 @@ struct StepHelp {
 // PW: pages each wave of the attention loads at once.
 template <int KT, int QT, int G, int KPT, int PW>
 __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A, StepPlan P) {
+  static_assert(G == 1, "one query head per kv-head: the merge is one wave's");
   __shared__ StepSmem<G> sm;
   __shared__ int32_t s_pt[kStepThreads * KPT];   // the list's page-table row
   // this chunk's share of the kept pages: (physical << 4) | (valid - 1), or -1
   __shared__ int32_t s_list[kStepMaxChunk];
   __shared__ uint32_t s_help[kStepMaxPages / kChunkGrain / 32];  // chunks whose keys are missing
-  __shared__ int s_last;
   const int tid = threadIdx.x;
   const int hq = A.hkv * G;
 
@@ -127,7 +126,10 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
 #pragma unroll
     for (int r = 0; r < KPT; ++r) s_pt[tid + kStepThreads * r] = ptv[r];
     for (int j = tid; j < (int)(sizeof(s_help) / sizeof(s_help[0])); j += kStepThreads) s_help[j] = 0u;
-    __syncthreads();  // s_pt and the clears before the selection
+    // s_pt and the clears before the selection (the selection's own first
+    // barrier would order them as well, but a common start of the waves' key
+    // reads measured faster)
+    __syncthreads();
 
     // 2. the list's selection (its keys re-read until all have arrived, or
     // scored here).  The kept pages are shared out by rank: chunk c attends to
@@ -158,18 +160,21 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     attend_range<KT, QT, G, PW, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b,
                                                   h, pt_row, L, nullptr, 0, hi - lo, A.scale_log2,
                                                   part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
-    // 4. arrival: every store of this task has completed before the count
+    // 4. arrival: every store of this task has completed before the count,
+    // which wave 0 takes; if it is the list's last chunk, wave 0 merges the
+    // list and returns its keys and counter to 0
     stores_done();
     __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(P.nc - 1);
-    __syncthreads();
-    if (s_last) {  // the list's last chunk: merge, then return keys and counter to 0
-      merge_list<true, 4>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim, sm.merge);
-      uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
-      for (int j = tid; j < A.max_pages; j += kStepThreads) st_x<true>(kw + j, 0u);
-      if (tid == 0) st_x<true>(A.arrive + i, 0u);
+    if (tid < 64) {
+      uint32_t prev = 0u;
+      if (tid == 0) prev = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
+      if (prev == (uint32_t)(P.nc - 1)) {
+        merge_list_wave<true>(part_list, P.nc, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim);
+        uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
+        for (int j = tid; j < A.max_pages; j += 64) st_x<true>(kw + j, 0u);
+        if (tid == 0) st_x<true>(A.arrive + i, 0u);
+      }
     }
     __syncthreads();  // shared memory is reused by the next task
   }
