@@ -517,50 +517,64 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
 // through lds (3 * blockDim floats).  The order is fixed, so the result is
 // deterministic.  COH: partials are read device-coherently (written by other
 // workgroups of the same launch).  All threads call.
-// merge_list for one query head (G = 1) by one wave, without LDS or barriers:
-// lane l folds output dimensions l and l + 64 over the ns records in order,
-// C records per memory round trip (the same arithmetic as merge_list's single
-// group).  Only the calling wave takes part.
-template <bool COH = false, int C = 8>
+// merge_list by one wave, without LDS or barriers: lane l folds output
+// dimensions l and l + 64 of each of the G query heads over the ns records
+// part[ns][G][kPartStride] in order, C records per memory round trip (the same
+// arithmetic as merge_list's single group).  Only the calling wave takes part.
+template <int G, bool COH = false, int C = (G <= 2 ? 8 : (G <= 8 ? 4 : 1))>
 __device__ __forceinline__ void merge_list_wave(const float* __restrict__ part, int ns,
                                                 float* __restrict__ out) {
   const int lane = threadIdx.x & 63;
-  float M = -INFINITY, a0 = 0.0f, a1 = 0.0f, lsum = 0.0f;
+  float M[G], a0[G], a1[G], lsum[G];
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    M[g] = -INFINITY;
+    a0[g] = a1[g] = lsum[g] = 0.0f;
+  }
   for (int s0 = 0; s0 < ns; s0 += C) {
-    float av0[C], av1[C], mv[C], lv[C];
+    float av0[C][G], av1[C][G], mv[C][G], lv[C][G];
 #pragma unroll
     for (int j = 0; j < C; ++j) {  // unconditional loads (clamped record) stay in flight together
-      const float* rec = part + (size_t)min(s0 + j, ns - 1) * kPartStride;
-      av0[j] = ld_x<COH>(rec + lane);
-      av1[j] = ld_x<COH>(rec + 64 + lane);
-      mv[j] = ld_x<COH>(rec + kHeadDim);
-      lv[j] = ld_x<COH>(rec + kHeadDim + 1);
-    }
 #pragma unroll
-    for (int j = 0; j < C; ++j)
-      if (s0 + j >= ns) lv[j] = 0.0f;
-    float Mc = M;
-#pragma unroll
-    for (int j = 0; j < C; ++j)
-      if (lv[j] > 0.0f) Mc = fmaxf(Mc, mv[j]);
-    if (Mc == -INFINITY) continue;  // nothing attended so far
-    const float r = exp2f(M - Mc);   // 0 when M is still -inf
-    a0 *= r;
-    a1 *= r;
-    lsum *= r;
-#pragma unroll
-    for (int j = 0; j < C; ++j) {
-      if (lv[j] > 0.0f) {
-        const float w = exp2f(mv[j] - Mc);
-        a0 = fmaf(av0[j], w, a0);
-        a1 = fmaf(av1[j], w, a1);
-        lsum = fmaf(lv[j], w, lsum);
+      for (int g = 0; g < G; ++g) {
+        const float* rec = part + ((size_t)min(s0 + j, ns - 1) * G + g) * kPartStride;
+        av0[j][g] = ld_x<COH>(rec + lane);
+        av1[j][g] = ld_x<COH>(rec + 64 + lane);
+        mv[j][g] = ld_x<COH>(rec + kHeadDim);
+        lv[j][g] = ld_x<COH>(rec + kHeadDim + 1);
       }
     }
-    M = Mc;
+#pragma unroll
+    for (int g = 0; g < G; ++g) {
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+        if (s0 + j >= ns) lv[j][g] = 0.0f;
+      float Mc = M[g];
+#pragma unroll
+      for (int j = 0; j < C; ++j)
+        if (lv[j][g] > 0.0f) Mc = fmaxf(Mc, mv[j][g]);
+      if (Mc == -INFINITY) continue;  // nothing attended so far
+      const float r = exp2f(M[g] - Mc);  // 0 when M is still -inf
+      a0[g] *= r;
+      a1[g] *= r;
+      lsum[g] *= r;
+#pragma unroll
+      for (int j = 0; j < C; ++j) {
+        if (lv[j][g] > 0.0f) {
+          const float w = exp2f(mv[j][g] - Mc);
+          a0[g] = fmaf(av0[j][g], w, a0[g]);
+          a1[g] = fmaf(av1[j][g], w, a1[g]);
+          lsum[g] = fmaf(lv[j][g], w, lsum[g]);
+        }
+      }
+      M[g] = Mc;
+    }
   }
-  out[lane] = lsum > 0.0f ? a0 / lsum : 0.0f;
-  out[64 + lane] = lsum > 0.0f ? a1 / lsum : 0.0f;
+#pragma unroll
+  for (int g = 0; g < G; ++g) {
+    out[g * kHeadDim + lane] = lsum[g] > 0.0f ? a0[g] / lsum[g] : 0.0f;
+    out[g * kHeadDim + 64 + lane] = lsum[g] > 0.0f ? a1[g] / lsum[g] : 0.0f;
+  }
 }
 
 template <bool COH = false, int C = 16>

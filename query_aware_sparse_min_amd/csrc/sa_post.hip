@@ -101,16 +101,32 @@ __global__ __launch_bounds__(64 * NW, 1) void post_score_kernel(PostArgs A, Post
       attend_range<KT, SA_BF16, G, PW, true, NW>(A.q, A.k, A.v, A.ks, A.vs, A.num_pages, A.hkv, b, h, pt_row,
                                                  L, nullptr, 0, hi - lo, A.scale_log2, part, sm.attn,
                                                  s_list);
-    // 4. arrival: every store of this task has completed before the count
+    // 4. arrival: every store of this task has completed before the count,
+    // which wave 0 takes; the list's last chunk merges the list and returns the
+    // counter to 0 (one or two query heads: wave 0 alone, measured faster;
+    // more: the whole workgroup, whose groups fold the records in parallel)
     stores_done();
     __syncthreads();
-    if (tid == 0)
-      s_last = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
-               (uint32_t)(P.nc - 1);
-    __syncthreads();
-    if (s_last) {  // the list's last chunk: merge, then return the counter to 0
-      merge_list<true, 4>(part_list, P.nc, G, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim, sm.merge);
-      if (tid == 0) st_x<true>(A.arrive + i, 0u);
+    float* out_row = A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim;
+    if constexpr (G <= 2) {
+      if (tid < 64) {
+        uint32_t prev = 0u;
+        if (tid == 0) prev = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
+        if (prev == (uint32_t)(P.nc - 1)) {
+          merge_list_wave<G, true>(part_list, P.nc, out_row);
+          if (tid == 0) st_x<true>(A.arrive + i, 0u);
+        }
+      }
+    } else {
+      if (tid == 0)
+        s_last = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) ==
+                 (uint32_t)(P.nc - 1);
+      __syncthreads();
+      if (s_last) {
+        merge_list<true, 4>(part_list, P.nc, G, out_row, sm.merge);
+        if (tid == 0) st_x<true>(A.arrive + i, 0u);
+      }
     }
     __syncthreads();  // shared memory is reused by the next task
   }

@@ -170,7 +170,7 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
       if (tid == 0) prev = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
       if (prev == (uint32_t)(P.nc - 1)) {
-        merge_list_wave<true>(part_list, P.nc, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim);
+        merge_list_wave<G, true>(part_list, P.nc, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim);
         uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
         for (int j = tid; j < A.max_pages; j += 64) st_x<true>(kw + j, 0u);
         if (tid == 0) st_x<true>(A.arrive + i, 0u);
