@@ -163,10 +163,15 @@ struct WavePages {
 // Folds the NW waves' (max, sum, acc) of every query head, which every wave
 // has stored to sm.m / sm.l / sm.acc, into the workgroup's partial records
 // part[G][kPartStride].  COH: stored device-coherently.  All threads call.
-template <int G, int NW, bool COH>
+// W0: wave 0 alone stores the records, and every wave's earlier stores have
+// completed at the barrier, so wave 0 can publish the records (wait for its
+// own stores, then signal) without another barrier.
+template <int G, int NW, bool COH, bool W0 = false>
 __device__ __forceinline__ void put_partials(AttnSmem<G, NW>& sm, float* __restrict__ part) {
+  if constexpr (W0) stores_done();
   __syncthreads();
-  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += blockDim.x) {
+  if (W0 && threadIdx.x >= 64) return;
+  for (int idx = threadIdx.x; idx < G * kHeadDim; idx += (W0 ? 64 : (int)blockDim.x)) {
     const int g = idx / kHeadDim, dim = idx % kHeadDim;
     float M = -INFINITY;
 #pragma unroll
@@ -196,7 +201,7 @@ __device__ __forceinline__ void put_partials(AttnSmem<G, NW>& sm, float* __restr
 // plain loads; the page table is then not read.
 // PW: pages each wave loads per iteration (PW * 8 row loads in flight per lane).
 // COH: lst is read and the partials are written device-coherently.
-template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4>
+template <int KT, int QT, int G, int PW = 2, bool COH = false, int NW = 4, bool W0 = false>
 __device__ __forceinline__ void attend_range(const void* __restrict__ q, const void* __restrict__ k,
                              const void* __restrict__ v, const uint16_t* __restrict__ ks,
                              const uint16_t* __restrict__ vs, int num_pages, int hkv, int b, int h,
@@ -309,7 +314,7 @@ __device__ __forceinline__ void attend_range(const void* __restrict__ q, const v
       }
     }
   }
-  put_partials<G, NW, COH>(sm, part);
+  put_partials<G, NW, COH, W0>(sm, part);
 }
 
 // ---------------------------------------------------------------- MFMA variant

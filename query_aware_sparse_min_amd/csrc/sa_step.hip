@@ -157,15 +157,15 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
 
     // 3. attention over the chunk's share of the kept pages
     float* part_list = A.partials + (size_t)i * P.nc * G * kPartStride;
-    attend_range<KT, QT, G, PW, true, kStepWaves>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b,
+    attend_range<KT, QT, G, PW, true, kStepWaves, true>(A.q, A.k, A.v, nullptr, nullptr, A.num_pages, A.hkv, b,
                                                   h, pt_row, L, nullptr, 0, hi - lo, A.scale_log2,
                                                   part_list + (size_t)c * G * kPartStride, sm.attn, s_list);
     // 4. arrival: every store of this task has completed before the count,
-    // which wave 0 takes; if it is the list's last chunk, wave 0 merges the
-    // list and returns its keys and counter to 0
-    stores_done();
-    __syncthreads();
+    // which wave 0 takes (the other waves' stores completed before the
+    // record's barrier, and wave 0 stored the record); if it is the list's
+    // last chunk, wave 0 merges the list and returns its keys and counter to 0
     if (tid < 64) {
+      stores_done();
       uint32_t prev = 0u;
       if (tid == 0) prev = __hip_atomic_fetch_add(A.arrive + i, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
       prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
