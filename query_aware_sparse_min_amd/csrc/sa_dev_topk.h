@@ -85,9 +85,15 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
   }
   const int m = n - n_head - n_tail;  // competing middle units; m > k >= 0
   const float* msc = sc + n_head;
-  const int run = (m + NT - 1) / NT;
-  const int r0 = min(tid * run, m);
-  const int cnt_t = min(run, m - r0);
+  // Scores (not KEYS) with KPT a multiple of 4: the runs are cut from the
+  // absolute units 0 .. n - 1, so that a run starts on a multiple of 4 units
+  // and is read with 16-byte loads; head and tail units inside a run are not
+  // keys.  Otherwise the runs are cut from the middle units.
+  constexpr bool kAbs = !KEYS && KPT > 0 && KPT % 4 == 0;
+  const int run = kAbs ? (n + NT - 1) / NT : (m + NT - 1) / NT;
+  const int r0 = kAbs ? min(tid * run, n) - n_head : min(tid * run, m);  // the run's first unit - n_head
+  const int j_lo = kAbs ? max(0, -r0) : 0;                          // keys j_lo .. cnt_t - 1
+  const int cnt_t = max(0, min(run, m - r0));
 
   // keys of the run: one round trip.  Loads are unconditional from clamped
   // in-range indices so that they are all in flight together; out-of-run
@@ -121,10 +127,21 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
     for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? key[j] : 0u;
   } else if constexpr (KPT > 0) {
     float v[KPT];
+    const float* rs = sc + (n_head + r0);  // kAbs: the run's first unit
+    if (kAbs && !COH && run % 4 == 0 && n_head + r0 + run <= n &&
+        (reinterpret_cast<uintptr_t>(rs) & 15u) == 0) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) v[j] = ld_x<COH>(msc + min(r0 + j, m - 1));
+      for (int j = 0; j < KPT; j += 4)
+        if (j < run) *reinterpret_cast<float4*>(&v[j]) = *reinterpret_cast<const float4*>(rs + j);
+    } else if (kAbs) {
 #pragma unroll
-    for (int j = 0; j < KPT; ++j) key[j] = j < cnt_t ? order_key(v[j]) : 0u;
+      for (int j = 0; j < KPT; ++j) v[j] = ld_x<COH>(sc + min(n_head + r0 + j, n - 1));
+    } else {
+#pragma unroll
+      for (int j = 0; j < KPT; ++j) v[j] = ld_x<COH>(msc + min(r0 + j, m - 1));
+    }
+#pragma unroll
+    for (int j = 0; j < KPT; ++j) key[j] = (j >= j_lo && j < cnt_t) ? order_key(v[j]) : 0u;
   }
   auto key_at = [&](int j) -> uint32_t {
     if constexpr (KPT > 0) return key[j];
@@ -134,7 +151,7 @@ __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, i
     if constexpr (KPT > 0) {
 #pragma unroll
       for (int j = 0; j < KPT; ++j)
-        if (j < cnt_t) f(j, key[j]);
+        if (j >= j_lo && j < cnt_t) f(j, key[j]);
     } else {
       for (int j = 0; j < cnt_t; ++j) f(j, key_at(j));
     }
