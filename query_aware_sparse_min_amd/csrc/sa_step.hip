@@ -43,7 +43,7 @@
 namespace sa {
 namespace {
 
-constexpr int kStepWaves = 12;              // one workgroup per CU: 12 waves, 168 VGPRs each
+constexpr int kStepWaves = 8;               // one workgroup per CU: 8 waves, up to 256 VGPRs each
 constexpr int kStepThreads = 64 * kStepWaves;
 constexpr int kScoreIT = (64 + kStepWaves - 1) / kStepWaves;  // load pairs per lane per score pass
 constexpr int kScorePass = 4 * kStepWaves * kScoreIT;          // pages per score pass (>= 256)
