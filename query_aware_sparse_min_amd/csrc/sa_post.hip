@@ -134,9 +134,10 @@ __global__ __launch_bounds__(64 * NW, 1) void post_score_kernel(PostArgs A, Post
 
 constexpr int kPostKpt = 4;  // register keys per thread for lists of up to 64 NW * 4 units
 
-// Waves per workgroup within the register budget of the group's attention: twelve
-// waves need at most 168 VGPRs, eight 256, four 512 (the 16-head accumulators).
-constexpr int post_waves(int G) { return G <= 2 ? 12 : (G <= 8 ? 8 : 4); }
+// Waves per workgroup within the register budget of the group's attention:
+// eight waves for up to eight heads (at most 256 VGPRs), four for 16 (the
+// 16-head accumulators take up to 512).
+constexpr int post_waves(int G) { return G <= 8 ? 8 : 4; }
 constexpr int post_threads(int G) { return 64 * post_waves(G); }
 
 template <int KT, int G>
