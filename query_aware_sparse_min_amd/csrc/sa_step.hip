@@ -163,7 +163,9 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
     // 4. arrival: every store of this task has completed before the count,
     // which wave 0 takes (the other waves' stores completed before the
     // record's barrier, and wave 0 stored the record); if it is the list's
-    // last chunk, wave 0 merges the list and returns its keys and counter to 0
+    // last chunk, wave 0 merges the list and returns its keys and counter to
+    // 0.  The keys are next read in the next launch, so plain stores (16 bytes
+    // per lane where the row allows) suffice: the launch boundary publishes them
     if (tid < 64) {
       stores_done();
       uint32_t prev = 0u;
@@ -171,8 +173,13 @@ __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A,
       prev = (uint32_t)__builtin_amdgcn_readfirstlane((int)prev);
       if (prev == (uint32_t)(P.nc - 1)) {
         merge_list_wave<G, true>(part_list, P.nc, A.out + ((size_t)b * hq + (size_t)h * G) * kHeadDim);
-        uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
-        for (int j = tid; j < A.max_pages; j += 64) st_x<true>(kw + j, 0u);
+        if (A.max_pages % 4 == 0) {
+          uint4* kw = reinterpret_cast<uint4*>(sc_row);
+          for (int j = tid; j < A.max_pages / 4; j += 64) kw[j] = make_uint4(0u, 0u, 0u, 0u);
+        } else {
+          uint32_t* kw = reinterpret_cast<uint32_t*>(sc_row);
+          for (int j = tid; j < A.max_pages; j += 64) kw[j] = 0u;
+        }
         if (tid == 0) st_x<true>(A.arrive + i, 0u);
       }
     }
