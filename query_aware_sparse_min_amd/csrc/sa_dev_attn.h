@@ -352,6 +352,33 @@ struct KOp8<SA_I8> {
   }
 };
 
+// The 32 consecutive K elements of a lane's row slice (four MFMA operands of
+// eight): bf16 as four 16-byte loads, int8 codes as two.
+template <int DT>
+struct KOp32;
+template <>
+struct KOp32<SA_BF16> {
+  KOp8<SA_BF16> o[4];
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) o[kk].load(base, e + 8 * kk);
+  }
+  __device__ __forceinline__ bf16x8_t get(int kk) const { return o[kk].get(); }
+};
+template <>
+struct KOp32<SA_I8> {
+  uint4 w[2];
+  __device__ __forceinline__ void load(const void* base, size_t e) {
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) w[hh] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(base) + e + 16 * hh);
+  }
+  __device__ __forceinline__ bf16x8_t get(int kk) const {
+    KOp8<SA_I8> o;
+    o.w = (kk & 1) ? make_uint2(w[kk >> 1].z, w[kk >> 1].w) : make_uint2(w[kk >> 1].x, w[kk >> 1].y);
+    return o.get();
+  }
+};
+
 // Value of lane g of each 16-lane row (DPP row_newbcast).
 template <int g>
 __device__ __forceinline__ float row_bcast(float v) {
@@ -428,42 +455,52 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
   const WavePages<false, NW> page_of(pt_row, lst, rlst, j0, j1, L, num_pages, jcap, masked);
   for (int jb = j0 + wave; jb < j1; jb += NW * PW) {
     PageRef pg[PW];
-    KOp8<KT> kr[PW][4];
+    KOp32<KT> kr[PW];
     Raw8<KT> vr[PW][4];
-    float ksc[PW][4], vsc[PW][4];
+    // int8: the K and V scales (fp16 bits) of token lane % 16 of the page; a
+    // lane takes those of its own tokens from the lanes that hold them
+    uint32_t kscw[PW], vscw[PW];
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
       pg[u] = page_of(jb + NW * u);
       const size_t ppl = pg[u].pp >= 0 ? (size_t)pg[u].pp : 0;  // empty slot: load page 0, result unused
       const size_t row = (ppl * kPage + tok_a) * hkv + h;
-#pragma unroll
-      for (int kk = 0; kk < 4; ++kk) kr[u][kk].load(k, row * kHeadDim + 32 * qg + 8 * kk);
+      kr[u].load(k, row * kHeadDim + 32 * qg);
 #pragma unroll
       for (int it = 0; it < 4; ++it) {
         const size_t tv = (ppl * kPage + 4 * it + r) * hkv + h;
         vr[u][it].load(v, tv * kHeadDim + 8 * c);
-        if constexpr (KT == SA_I8) {
-          ksc[u][it] = f16_to_f32(ks[(ppl * kPage + 4 * it + qg) * hkv + h]);
-          vsc[u][it] = f16_to_f32(vs[tv]);
-        } else {
-          ksc[u][it] = vsc[u][it] = 1.0f;
-        }
+      }
+      if constexpr (KT == SA_I8) {
+        const size_t ts = (ppl * kPage + (lane & 15)) * hkv + h;
+        kscw[u] = ks[ts];
+        vscw[u] = vs[ts];
       }
     }
     // every load of the iteration is issued before any of them is used
     __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
     for (int u = 0; u < PW; ++u) {
+      float ksc[4], vsc[4];  // tokens 4 i + qg
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if constexpr (KT == SA_I8) {
+          ksc[i] = f16_to_f32((uint16_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + qg), (int)kscw[u]));
+          vsc[i] = f16_to_f32((uint16_t)__builtin_amdgcn_ds_bpermute(4 * (4 * i + qg), (int)vscw[u]));
+        } else {
+          ksc[i] = vsc[i] = 1.0f;
+        }
+      }
       f32x4_t z = {0.0f, 0.0f, 0.0f, 0.0f};
 #pragma unroll
       for (int kk = 0; kk < 4; ++kk)
-        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[u][kk].get(), qb[kk], z, 0, 0, 0);
+        z = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kr[u].get(kk), qb[kk], z, 0, 0, 0);
 
       const bool live = pg[u].pp >= 0 && n < G && ((pg[u].mask >> n) & 1u);
       float zz[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i)  // token 4 i + qg
-        zz[i] = (live && 4 * i + qg < pg[u].nv) ? z[i] * (scale_log2 * ksc[u][i]) : -INFINITY;
+        zz[i] = (live && 4 * i + qg < pg[u].nv) ? z[i] * (scale_log2 * ksc[i]) : -INFINITY;
       float pm = fmaxf(fmaxf(zz[0], zz[1]), fmaxf(zz[2], zz[3]));
       pm = pair32_max(pair16_max(pm));  // over the page's 16 tokens, for head n
       const float mn = fmaxf(mrun, pm);
@@ -480,7 +517,7 @@ __device__ __forceinline__ void attend_range_mfma(const void* __restrict__ q,
         const float ag = row_bcast<g>(alpha);
         float pw[4];
 #pragma unroll
-        for (int it = 0; it < 4; ++it) pw[it] = row_bcast<g>(p[it]) * vsc[u][it];
+        for (int it = 0; it < 4; ++it) pw[it] = row_bcast<g>(p[it]) * vsc[it];
 #pragma unroll
         for (int e = 0; e < 8; ++e) acc[g][e] *= ag;
 #pragma unroll
