@@ -75,7 +75,7 @@ struct StepHelp {
   }
 };
 
-// KPT: top-K keys per thread in registers (lists of up to 768 * KPT pages).
+// KPT: top-K keys per thread in registers (lists of up to kStepThreads * KPT pages).
 // PW: pages each wave of the attention loads at once.
 template <int KT, int QT, int G, int KPT, int PW>
 __global__ __launch_bounds__(kStepThreads, 1) void quest_step_kernel(StepArgs A, StepPlan P) {

@@ -50,12 +50,12 @@ CASES = {
     # a list of 18750 pages: the top-K that re-reads its keys from the scores
     "gqa2_bf16_18k_pages": dict(B=1, Hq=2, Hkv=1, lens=(300000,), kv_dtype="bf16",
                                 q_dtype="bf16", budget_pages=64),
-    # the fused step with lists of 2305..4096 pages (six register keys per thread):
+    # the fused step with lists of 2049..4096 pages (eight register keys per thread):
     # one query head per kv-head, Quest, random page tables, bf16 and fp32
-    "mha_bf16_64k_kpt6": dict(B=2, Hq=2, Hkv=2, lens=(65536, 40000), kv_dtype="bf16",
-                              q_dtype="bf16", budget_pages=200, page_table="random"),
-    "mha_f32_64k_kpt6": dict(B=2, Hq=2, Hkv=2, lens=(65536, 40000), kv_dtype="f32",
-                             q_dtype="f32", budget_pages=130, page_table="random"),
+    "mha_bf16_64k_kpt_hi": dict(B=2, Hq=2, Hkv=2, lens=(65536, 40000), kv_dtype="bf16",
+                                q_dtype="bf16", budget_pages=200, page_table="random"),
+    "mha_f32_64k_kpt_hi": dict(B=2, Hq=2, Hkv=2, lens=(65536, 40000), kv_dtype="f32",
+                               q_dtype="f32", budget_pages=130, page_table="random"),
 }
 
 
