@@ -369,8 +369,9 @@ template <>
 struct KOp32<SA_I8> {
   uint4 w[2];
   __device__ __forceinline__ void load(const void* base, size_t e) {
+    const int8_t* p = static_cast<const int8_t*>(base) + e;
 #pragma unroll
-    for (int hh = 0; hh < 2; ++hh) w[hh] = *reinterpret_cast<const uint4*>(static_cast<const int8_t*>(base) + e + 16 * hh);
+    for (int hh = 0; hh < 2; ++hh) w[hh] = *reinterpret_cast<const uint4*>(p + 16 * hh);
   }
   __device__ __forceinline__ bf16x8_t get(int kk) const {
     KOp8<SA_I8> o;

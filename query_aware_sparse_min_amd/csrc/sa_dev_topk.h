@@ -69,8 +69,9 @@ struct TopkSmem {
 // order_key() words written by other workgroups, 0 while not yet written; such
 // words are re-read for up to kKeyWaitTicks, and any still missing then are
 // produced through help (so the call never depends on another workgroup
-// being resident).  With k = 0 the keys are not needed and nothing is waited for.  All NT threads call; sm is free again on return once the
-// caller has synchronised.
+// being resident).  With k = 0 the keys are not needed and nothing is waited
+// for.  All NT threads call; sm is free again on return once the caller has
+// synchronised.
 template <int NT, int KPT, bool COH, bool KEYS = false, typename Keep, typename Help = NoHelp>
 __device__ __forceinline__ void topk_core(const float* __restrict__ sc, int n, int k, int n_head,
                                           int n_tail, TopkSmem<NT>& sm, Keep&& keep,

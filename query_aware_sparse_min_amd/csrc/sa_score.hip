@@ -393,8 +393,11 @@ __global__ __launch_bounds__(256, G >= 16 ? 3 : 4) void sals_score_kernel(
     for (int blk = 0; blk < 2; ++blk) {
       // the 8 token slots of kv-head x: lanes x + 8 k
       float mb = m[blk], sb = s[blk];
-      lse_merge(mb, sb, __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(mb), 0x128, 0xF, 0xF, false)),
-                __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(sb), 0x128, 0xF, 0xF, false)));
+      auto ror8 = [](float v) {  // DPP row_ror:8
+        return __uint_as_float((uint32_t)__builtin_amdgcn_update_dpp(0, (int)__float_as_uint(v), 0x128, 0xF, 0xF,
+                                                                     false));
+      };
+      lse_merge(mb, sb, ror8(mb), ror8(sb));
       {
         const auto rm = __builtin_amdgcn_permlane16_swap(__float_as_uint(mb), __float_as_uint(mb), false, false);
         const auto rs = __builtin_amdgcn_permlane16_swap(__float_as_uint(sb), __float_as_uint(sb), false, false);
