@@ -119,10 +119,12 @@ __device__ __forceinline__ void attn_task(
   const int j0 = split * pps, j1 = min(j0 + pps, cnt);
   // the split's list entries are read together with the list length
   const int jcap = sel ? min(j0 + pps, max_sel) : -1;
-  // four or more bf16 query heads per kv-head: scores on the matrix cores
+  // four or more bf16 query heads per kv-head: scores on the matrix cores, two
+  // pages per wave in flight up to eight heads (sixteen: one, for registers)
   if constexpr (G >= 4 && QT == SA_BF16 && (KT == SA_BF16 || KT == SA_I8))
-    attend_range_mfma<KT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
-                             lst, j0, j1, scale_log2, part, sm, jcap, masked != 0);
+    attend_range_mfma<KT, G, 4, (G <= 8 ? 2 : 1)>(q, k, v, ks, vs, num_pages, hkv, b, h,
+                                                 pt + (size_t)b * max_pages, L, lst, j0, j1, scale_log2,
+                                                 part, sm, jcap, masked != 0);
   else
     attend_range<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, b, h, pt + (size_t)b * max_pages, L,
                             lst, j0, j1, scale_log2, part, sm, nullptr, jcap, masked != 0);
