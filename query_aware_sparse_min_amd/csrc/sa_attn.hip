@@ -102,8 +102,9 @@ __device__ __forceinline__ void ragged_task(const int* pre, int B, int hkv, int 
 
 // One split of one (batch, kv-head) list: pages [split * pps, + pps) of the
 // sequence (sel == nullptr) or of its selected list, into the partial records
-// part[G][kPartStride].
-template <int KT, int QT, int G>
+// part[G][kPartStride].  MPW: pages per wave in flight with the matrix-core
+// scores (2 for the long splits of the dense device plan).
+template <int KT, int QT, int G, int MPW = 1>
 __device__ __forceinline__ void attn_task(
     const void* __restrict__ q, const void* __restrict__ k, const void* __restrict__ v,
     const uint16_t* __restrict__ ks, const uint16_t* __restrict__ vs, int num_pages, int hkv,
@@ -119,10 +120,10 @@ __device__ __forceinline__ void attn_task(
   const int j0 = split * pps, j1 = min(j0 + pps, cnt);
   // the split's list entries are read together with the list length
   const int jcap = sel ? min(j0 + pps, max_sel) : -1;
-  // four or more bf16 query heads per kv-head: scores on the matrix cores, two
-  // pages per wave in flight up to eight heads (sixteen: one, for registers)
+  // four or more bf16 query heads per kv-head: scores on the matrix cores
+  // (sixteen heads: one page per wave in flight, for registers)
   if constexpr (G >= 4 && QT == SA_BF16 && (KT == SA_BF16 || KT == SA_I8))
-    attend_range_mfma<KT, G, 4, (G <= 8 ? 2 : 1)>(q, k, v, ks, vs, num_pages, hkv, b, h,
+    attend_range_mfma<KT, G, 4, (G <= 8 ? MPW : 1)>(q, k, v, ks, vs, num_pages, hkv, b, h,
                                                  pt + (size_t)b * max_pages, L, lst, j0, j1, scale_log2,
                                                  part, sm, jcap, masked != 0);
   else
@@ -152,9 +153,9 @@ __global__ __launch_bounds__(kAttnThreads) void attn_kernel(
     if (t >= rp.tasks) return;
     int b, h, split;
     ragged_task(pre, B, hkv, t, b, h, split);
-    attn_task<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, pt, max_pages, sel, num_sel, max_sel, b, h,
-                         split, rp.pps, len_s[b], scale_log2,
-                         partials + (size_t)t * G * kPartStride, masked, sm);
+    attn_task<KT, QT, G, 2>(q, k, v, ks, vs, num_pages, hkv, pt, max_pages, sel, num_sel, max_sel, b, h,
+                            split, rp.pps, len_s[b], scale_log2,
+                            partials + (size_t)t * G * kPartStride, masked, sm);
   } else {
     const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z;
     attn_task<KT, QT, G>(q, k, v, ks, vs, num_pages, hkv, pt, max_pages, sel, num_sel, max_sel, b, h,
